@@ -1,0 +1,339 @@
+"""Pins for the float64 oracle: each check compares the oracle with something
+that is not the oracle (the pages' worked example, brute force in pure Python,
+a library routine, closed forms, invariants). Every check raises
+AssertionError on failure; tests/test_oracle.py runs them, and
+tests/test_oracle_mutations.py plants mistakes in the oracle and expects one
+of them to fail.
+
+The oracle is always reached through the module attribute (``O.name``) so a
+planted mistake is seen by every caller.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ------------------------------------------------------------------ plan
+
+def check_plan_golden():
+    with open(os.path.join(GOLDEN, "plan_token_ranges.json")) as f:
+        spec = json.load(f)
+    for case in spec["cases"]:
+        got = O.plan_shards(case["seq_lens"], case["num_shards"], case["block_size"])
+        assert got.tolist() == case["bounds"], (case, got.tolist())
+
+
+def _plan_brute(L, S, bs):
+    """Smallest per-shard page budget that fits, found by search; shards filled in order."""
+    pages = 0
+    while pages * bs < L:
+        pages += 1
+    k = 0
+    while k * S < pages:
+        k += 1
+    out, pos = [], 0
+    for _ in range(S):
+        take = min(k, pages - pos)
+        a = min(L, pos * bs)
+        pos += take
+        out.append((a, min(L, pos * bs)))
+    return out
+
+
+def check_plan_brute(rng=None):
+    rng = rng or np.random.default_rng(7)
+    cases = [(0, 3, 16), (1, 8, 64), (15, 4, 16), (16, 4, 16), (17, 4, 16), (63, 8, 64),
+             (1_000_000, 16, 16), (800_000, 16, 16), (500_000, 16, 16), (200_000, 16, 16)]
+    cases += [(int(rng.integers(0, 5000)), int(rng.integers(1, 33)), int(rng.choice([1, 16, 64])))
+              for _ in range(300)]
+    for L, S, bs in cases:
+        got = O.plan_shards([L], S, bs)[0].tolist()
+        exp = [list(x) for x in _plan_brute(L, S, bs)]
+        assert got == exp, (L, S, bs, got, exp)
+        # contiguous cover of [0, L), page-aligned interior cuts
+        assert got[0][0] == 0 and got[-1][1] == L
+        for (a0, a1), (b0, _) in zip(got, got[1:]):
+            assert a1 == b0 and a0 <= a1
+            assert a1 % bs == 0 or a1 == L
+
+
+# ------------------------------------------------------------------ gather
+
+def check_gather_example():
+    """bs 4, block table [2, 0, 3]: tokens 0..9 live at (page, slot) listed by hand."""
+    bs, N, Hkv = 4, 4, 2
+    cache = np.zeros((N, Hkv, bs, 3), dtype=np.float32)
+    for p in range(N):
+        for h in range(Hkv):
+            for s in range(bs):
+                cache[p, h, s] = (p, h, s)
+    table = np.array([[2, 0, 3]], dtype=np.int32)
+    want = [(2, 0), (2, 1), (2, 2), (2, 3), (0, 0), (0, 1), (0, 2), (0, 3), (3, 0), (3, 1)]
+    rows = O.gather_gqa(cache, table, 0, 1, 0, 10, bs)
+    assert [(int(r[0]), int(r[2])) for r in rows] == want
+    assert all(int(r[1]) == 1 for r in rows)
+    rows = O.gather_gqa(cache, table, 0, 0, 3, 9, bs)
+    assert [(int(r[0]), int(r[2])) for r in rows] == want[3:9]
+    mla = cache[:, 0]  # [N, bs, 3]
+    rows = O.gather_mla(mla, table, 0, 5, 10, bs)
+    assert [(int(r[0]), int(r[2])) for r in rows] == want[5:10]
+
+
+def check_gather_fast_matches():
+    rng = np.random.default_rng(3)
+    bs, N, Hkv, D = 16, 40, 3, 5
+    cache = rng.standard_normal((N, Hkv, bs, D))
+    table = rng.permutation(N).reshape(2, 20).astype(np.int32)
+    for _ in range(50):
+        b = int(rng.integers(0, 2))
+        a = int(rng.integers(0, 320))
+        e = int(rng.integers(a, 321))
+        g = int(rng.integers(0, Hkv))
+        assert np.array_equal(O._gather_fast(cache, table, b, a, e, bs, g),
+                              O.gather_gqa(cache, table, b, g, a, e, bs))
+        assert np.array_equal(O._gather_fast(cache[:, g], table, b, a, e, bs),
+                              O.gather_mla(cache[:, g], table, b, a, e, bs))
+
+
+def check_gather_permutation_invariant():
+    """Relabelling physical pages (and the table with them) changes nothing."""
+    rng = np.random.default_rng(4)
+    bs, N, D = 8, 12, 4
+    cache = rng.standard_normal((N, bs, D))
+    table = rng.permutation(N).reshape(2, 6).astype(np.int32)
+    perm = rng.permutation(N)
+    cache2 = np.empty_like(cache)
+    cache2[perm] = cache
+    table2 = perm[table].astype(np.int32)
+    for b in range(2):
+        assert np.array_equal(O.gather_mla(cache, table, b, 3, 45, bs),
+                              O.gather_mla(cache2, table2, b, 3, 45, bs))
+
+
+# ------------------------------------------------------------------ attention
+
+def _brute_attention(q, k, v, scale):
+    """Pure-Python softmax attention with math.fsum (exact-sum) reductions."""
+    H, n = len(q), len(k)
+    out, lses = [], []
+    for h in range(H):
+        s = [scale * math.fsum(q[h][d] * k[t][d] for d in range(len(q[h]))) for t in range(n)]
+        m = max(s)
+        tot = math.fsum(math.exp(x - m) for x in s)
+        lse = m + math.log(tot)
+        w = [math.exp(x - lse) for x in s]
+        out.append([math.fsum(w[t] * v[t][j] for t in range(n)) for j in range(len(v[0]))])
+        lses.append(lse)
+    return np.array(out), np.array(lses)
+
+
+def check_attention_brute():
+    rng = np.random.default_rng(11)
+    for n in (1, 2, 5, 12):
+        for d in (1, 3, 5):
+            q = rng.standard_normal((2, d))
+            k = rng.standard_normal((n, d)) * 2
+            v = rng.standard_normal((n, 4))
+            o, lse = O.attention(q, k, v, 0.7)
+            eo, el = _brute_attention(q.tolist(), k.tolist(), v.tolist(), 0.7)
+            assert np.allclose(o, eo, rtol=1e-12, atol=1e-13), (n, d)
+            assert np.allclose(lse, el, rtol=1e-13, atol=1e-13), (n, d)
+
+
+def check_attention_library():
+    """torch's scaled_dot_product_attention and logsumexp in float64 on CPU."""
+    import torch
+    rng = np.random.default_rng(12)
+    for n, D, Dv in ((7, 16, 16), (300, 64, 64), (129, 576, 512)):
+        q = rng.standard_normal((8, D))
+        k = rng.standard_normal((n, D))
+        v = rng.standard_normal((n, Dv))
+        scale = 1.0 / math.sqrt(D)
+        o, lse = O.attention(q, k, v, scale)
+        tq = torch.from_numpy(q)[None, :, None, :]
+        tk = torch.from_numpy(k)[None, None].expand(1, 8, n, D)
+        tv = torch.from_numpy(v)[None, None].expand(1, 8, n, Dv)
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale)[0, :, 0]
+        ref_lse = torch.logsumexp(scale * (torch.from_numpy(q) @ torch.from_numpy(k).T), dim=1)
+        assert np.allclose(o, ref.numpy(), rtol=1e-10, atol=1e-12)
+        assert np.allclose(lse, ref_lse.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def check_attention_closed_forms():
+    rng = np.random.default_rng(13)
+    # all keys equal: uniform weights, O = mean(V), LSE = s + ln n
+    q = rng.standard_normal((3, 6))
+    k1 = rng.standard_normal(6)
+    n = 37
+    k = np.tile(k1, (n, 1))
+    v = rng.standard_normal((n, 5))
+    o, lse = O.attention(q, k, v, 0.4)
+    s = 0.4 * (q @ k1)
+    assert np.allclose(o, np.tile(v.mean(axis=0), (3, 1)), rtol=1e-12, atol=1e-13)
+    assert np.allclose(lse, s + math.log(n), rtol=1e-13, atol=1e-13)
+    # one score 1000 above the rest: O = v_j, LSE = s_j
+    q = np.zeros((1, 2)); q[0, 0] = 1.0
+    k = rng.standard_normal((9, 2)) * 0.1
+    j = 4
+    k[j, 0] = 1000.0
+    v = rng.standard_normal((9, 3))
+    o, lse = O.attention(q, k, v, 1.0)
+    assert np.array_equal(o[0], v[j])
+    assert abs(lse[0] - k[j, 0]) < 1e-9
+    # empty range
+    o, lse = O.attention(q, k[:0], v[:0], 1.0)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def check_attention_laws():
+    rng = np.random.default_rng(14)
+    q = rng.standard_normal((4, 8))
+    k = rng.standard_normal((20, 8))
+    v = rng.standard_normal((20, 6))
+    o, lse = O.attention(q, k, v, 0.3)
+    # V-affine: O(aV + b) = a O + b
+    o2, lse2 = O.attention(q, k, 2.5 * v + 1.25, 0.3)
+    assert np.allclose(o2, 2.5 * o + 1.25, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(lse, lse2)
+    # the scale multiplies the scores: scale c on q == scale 1 on c*q
+    o3, lse3 = O.attention(0.3 * q, k, v, 1.0)
+    assert np.allclose(o3, o, rtol=1e-12, atol=1e-13) and np.allclose(lse3, lse, rtol=1e-13)
+    # weights sum to one: V = all-ones gives O = 1
+    o4, _ = O.attention(q, k, np.ones_like(v), 0.3)
+    assert np.allclose(o4, 1.0, rtol=1e-13)
+
+
+# ------------------------------------------------------------------ merge
+
+def _random_partition(n, S, rng, allow_empty=True):
+    cuts = np.sort(rng.integers(0 if allow_empty else 1, n + 1, size=S - 1))
+    edges = [0] + cuts.tolist() + [n]
+    return list(zip(edges[:-1], edges[1:]))
+
+
+def check_merge_partition_invariance():
+    rng = np.random.default_rng(15)
+    for trial in range(40):
+        n = int(rng.integers(1, 200))
+        q = rng.standard_normal((5, 7))
+        k = rng.standard_normal((n, 7)) * (3 if trial % 2 else 1)
+        v = rng.standard_normal((n, 4))
+        full_o, full_lse = O.attention(q, k, v, 0.5)
+        kinds = [1, n, int(rng.integers(1, 40))]
+        for S in kinds:
+            parts = ([(t, t + 1) for t in range(n)] if S == n else _random_partition(n, S, rng))
+            po = np.stack([O.attention(q, k[a:b], v[a:b], 0.5)[0] for a, b in parts])
+            pl = np.stack([O.attention(q, k[a:b], v[a:b], 0.5)[1] for a, b in parts])
+            mo, ml = O.merge_lse(po, pl)
+            assert np.allclose(mo, full_o, rtol=1e-11, atol=1e-12), (trial, S)
+            assert np.allclose(ml, full_lse, rtol=1e-12, atol=1e-12), (trial, S)
+
+
+def check_merge_associative_and_edge_cases():
+    rng = np.random.default_rng(16)
+    po = rng.standard_normal((6, 3, 4))
+    pl = rng.standard_normal((6, 3)) * 5
+    pl[2] = -np.inf
+    po[2] = 0.0
+    o, lse = O.merge_lse(po, pl)
+    oa, la = O.merge_lse(po[:3], pl[:3])
+    ob, lb = O.merge_lse(po[3:], pl[3:])
+    o2, l2 = O.merge_lse(np.stack([oa, ob]), np.stack([la, lb]))
+    assert np.allclose(o, o2, rtol=1e-12, atol=1e-13) and np.allclose(lse, l2, rtol=1e-13)
+    # single shard: identity
+    o1, l1 = O.merge_lse(po[:1], pl[:1])
+    assert np.allclose(o1, po[0], rtol=1e-14, atol=0) and np.allclose(l1, pl[0], rtol=1e-14)
+    # two shards with equal LSE: plain average, LSE + ln 2
+    a, b = rng.standard_normal((3, 4)), rng.standard_normal((3, 4))
+    lsev = rng.standard_normal(3)
+    o, lse = O.merge_lse(np.stack([a, b]), np.stack([lsev, lsev]))
+    assert np.allclose(o, (a + b) / 2, rtol=1e-13, atol=1e-14)
+    assert np.allclose(lse, lsev + math.log(2.0), rtol=1e-13, atol=1e-14)
+    # all shards empty
+    o, lse = O.merge_lse(np.zeros((4, 3, 2)), np.full((4, 3), -np.inf))
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+# ------------------------------------------------------------------ whole path
+
+def check_gqa_head_groups():
+    """Query head h reads KV head h // G: give KV head g all values equal to g."""
+    bs, Hkv, G, D = 4, 3, 2, 4
+    N = 6
+    rng = np.random.default_rng(17)
+    k = rng.standard_normal((N, Hkv, bs, D)).astype(np.float32)
+    v = np.zeros((N, Hkv, bs, D), dtype=np.float32)
+    for g in range(Hkv):
+        v[:, g] = g
+    q = rng.standard_normal((1, Hkv * G, D)).astype(np.float32)
+    table = np.array([[5, 1, 3]], dtype=np.int32)
+    o, lse = O.full_attention("gqa", "f32", q, (k, v), table, [11], bs, 0.5, D)
+    for h in range(Hkv * G):
+        assert np.allclose(o[0, h], h // G, atol=1e-12), h
+
+
+def check_mla_value_is_latent_prefix():
+    """MLA V = first Dv dims of the cached row; rope dims only enter scores."""
+    rng = np.random.default_rng(18)
+    bs, N, Dqk, Dv = 4, 5, 10, 6
+    cache = rng.standard_normal((N, bs, Dqk)).astype(np.float32)
+    table = np.array([[4, 2, 0]], dtype=np.int32)
+    q = rng.standard_normal((1, 3, Dqk)).astype(np.float32)
+    L = 10
+    o, lse = O.full_attention("mla", "f32", q, (cache,), table, [L], bs, 0.8, Dv)
+    rows = np.stack([cache[table[0, t // bs], t % bs] for t in range(L)]).astype(np.float64)
+    eo, el = _brute_attention(q[0].astype(np.float64).tolist(), rows.tolist(),
+                              rows[:, :Dv].tolist(), 0.8)
+    assert np.allclose(o[0], eo, rtol=1e-12, atol=1e-13)
+    assert np.allclose(lse[0], el, rtol=1e-13)
+
+
+def check_sharded_equals_full():
+    """The DCP result (plan, partials, merge) equals unsharded attention."""
+    from workloads import workload, make_host_inputs
+    wl = workload("gqa-tiny")
+    inp = make_host_inputs(wl)
+    args = (wl.kind, wl.dtype, inp["q"], (inp["k_cache"], inp["v_cache"]), inp["block_table"])
+    bounds, po, pl, o, lse = O.sharded_attention(*args, inp["seq_lens"], wl.num_shards,
+                                                 wl.block_size, wl.softmax_scale, wl.head_dim_v)
+    fo, fl = O.full_attention(*args, inp["seq_lens"], wl.block_size, wl.softmax_scale,
+                              wl.head_dim_v)
+    assert bounds[:, :, 1].tolist() == [[256, 512, 768, 1024]] * 2
+    assert np.allclose(o, fo, rtol=1e-11, atol=1e-12)
+    assert np.allclose(lse, fl, rtol=1e-12, atol=1e-12)
+
+
+def check_bf16_upcast():
+    bits = np.array([0x3F80, 0xC000, 0x3F00, 0x0001, 0x7F7F, 0x8000, 0x4049], dtype=np.uint16)
+    want = [1.0, -2.0, 0.5, 2.0 ** -133, (2 - 2 ** -7) * 2.0 ** 127, -0.0, 3.140625]
+    got = O.bf16_bits_to_f64(bits)
+    assert got.tolist() == want
+    assert math.copysign(1.0, got[5]) == -1.0
+
+
+ALL_CHECKS = [
+    check_bf16_upcast,
+    check_plan_golden,
+    check_plan_brute,
+    check_gather_example,
+    check_gather_fast_matches,
+    check_gather_permutation_invariant,
+    check_attention_brute,
+    check_attention_library,
+    check_attention_closed_forms,
+    check_attention_laws,
+    check_merge_partition_invariance,
+    check_merge_associative_and_edge_cases,
+    check_gqa_head_groups,
+    check_mla_value_is_latent_prefix,
+    check_sharded_equals_full,
+]

@@ -1,0 +1,18 @@
+"""Seeded synthetic inputs for sequence-sharded paged decode attention.
+
+This package only draws inputs (context lengths, page pools and block tables,
+queries, KV caches, planted keys). It holds none of the attention arithmetic,
+no shard plan and no kernel logic; the CPU oracle and the GPU path both consume
+what it produces.
+"""
+
+from .configs import (  # noqa: F401
+    WORKLOADS,
+    Workload,
+    bf16_bits_from_f32,
+    draw_block_table,
+    draw_lengths,
+    make_device_inputs,
+    make_host_inputs,
+    workload,
+)
