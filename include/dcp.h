@@ -1,0 +1,204 @@
+/*
+ * dcp.h -- sequence-sharded paged decode attention for MI355X (gfx950).
+ *
+ * The operation is the decode-time step of Decode Context Parallelism:
+ *
+ *  1. The KV cache of each request is split along the sequence into
+ *     contiguous token shards [start, end); each DCP rank owns one range
+ *     (Qiita article on vLLM -dcp, section on assigning token ranges to GPUs;
+ *     naphjohn blog "Inference Systems Infrastructure Notes (7)", section 2).
+ *  2. The one-token decode query attends over each shard's KV only, giving a
+ *     partial result: the shard's softmax output O_s and its log-sum-exp
+ *     LSE_s (same Qiita section, second step of its three).
+ *  3. The partials are combined by online-softmax re-weighting into exactly
+ *     the attention over the whole context (same Qiita section, third step;
+ *     blog section 2):  M = max_s LSE_s,  LSE = M + ln sum_s exp(LSE_s - M),
+ *     O = sum_s exp(LSE_s - LSE) * O_s.
+ *  4. The intermediate partials live in one caller-owned workspace that is
+ *     reused every step instead of being allocated per call (blog section 3,
+ *     scratch-buffer reuse).
+ *
+ * On one GPU every shard of every request is resident; the shards stand in
+ * for the ranks of a DCP group and no collective is issued.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every entry point returns a dcp_status. Host-checkable problems (NULL
+ *    or misaligned pointers, sizes, unsupported shapes, workspace too small)
+ *    are reported before any device work is queued. Nothing throws across
+ *    this ABI. dcp_last_error() returns a thread-local detail string for the
+ *    last failing call on the calling thread.
+ *  - Device entry points queue kernels on `stream` (a hipStream_t passed as
+ *    void*; NULL means the legacy default stream) and never synchronise.
+ *  - All memory is owned by the caller. The library allocates no device
+ *    memory and keeps no state beyond a per-device cache of launch
+ *    parameters and the thread-local error string.
+ *  - Device pointers to Q, caches, partials, outputs and workspace must be
+ *    16-byte aligned (the kernels use 128-bit loads and stores).
+ *  - Values that only exist on the device (bounds, block-table entries) are
+ *    checked by the kernels without faulting: a bound outside
+ *    [0, max_blocks_per_seq * block_size] is clamped, a block id outside
+ *    [0, num_blocks) is treated as a page of masked tokens, and either event
+ *    sets a sticky bit in the workspace (dcp_read_device_flags).
+ */
+#ifndef DCP_H_
+#define DCP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DCP_ABI_VERSION 1
+
+typedef int32_t dcp_status;
+enum {
+  DCP_OK = 0,
+  DCP_ERR_NULL = 1,        /* a required pointer is NULL */
+  DCP_ERR_SHAPE = 2,       /* sizes out of range or inconsistent */
+  DCP_ERR_UNSUPPORTED = 3, /* valid request that no kernel implements */
+  DCP_ERR_WORKSPACE = 4,   /* workspace smaller than dcp_workspace_bytes() */
+  DCP_ERR_BAD_PLAN = 5,    /* host-visible sequence lengths are invalid (negative) */
+  DCP_ERR_ALIGN = 6,       /* a device pointer is not 16-byte aligned */
+  DCP_ERR_DEVICE = 7       /* the HIP runtime reported an error */
+};
+
+/* Element type of Q and of the KV cache (both the same). */
+enum { DCP_F32 = 0, DCP_BF16 = 1 };
+
+/* Cache layout.
+ * DCP_KV_GQA: separate K and V caches, each [num_blocks][num_kv_heads][block_size][head_dim]
+ *             (one KV head of one page is a contiguous block_size x head_dim tile).
+ *             head_dim_qk == head_dim_v. Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * DCP_KV_MLA: one latent cache [num_blocks][block_size][head_dim_qk] shared by all query heads
+ *             (num_kv_heads == 1); the value of a token is the first head_dim_v entries of its
+ *             cached row (absorbed MLA: 576 = 512 latent + 64 rope, value 512). v_cache is NULL.
+ * Token t of request b is in page block_table[b * max_blocks_per_seq + t / block_size], at slot
+ * t % block_size (paged KV, vLLM's PagedAttention blocks). */
+enum { DCP_KV_GQA = 0, DCP_KV_MLA = 1 };
+
+typedef struct dcp_attn_shape {
+  int32_t batch;              /* B >= 1 requests, one decode query token each */
+  int32_t num_q_heads;        /* Hq */
+  int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0; 1 for MLA */
+  int32_t head_dim_qk;        /* Dqk: dims of q and k */
+  int32_t head_dim_v;         /* Dv: dims of v and of the output */
+  int32_t block_size;         /* tokens per KV page */
+  int32_t max_blocks_per_seq; /* row length of block_table */
+  int32_t num_blocks;         /* pages in the cache pool */
+  int32_t num_shards;         /* S shards per request */
+  int32_t dtype;              /* DCP_F32 or DCP_BF16, for q and caches */
+  int32_t kv_kind;            /* DCP_KV_GQA or DCP_KV_MLA */
+  float softmax_scale;        /* scores are softmax_scale * <q, k> */
+} dcp_attn_shape;
+
+/* DCP_ABI_VERSION of the loaded library. */
+int32_t dcp_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* dcp_status_string(dcp_status status);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* dcp_last_error(void);
+
+/*
+ * dcp_plan_shards -- host only, no device work.
+ * The canonical split of each request into num_shards contiguous token ranges that start on
+ * page boundaries (Qiita section on token ranges: 200K tokens over 4 ranks gives 0-50K,
+ * 50K-100K, ...). With P = ceil(L / block_size) pages and k = ceil(P / num_shards):
+ *   start_s = min(L, s*k*block_size),  end_s = min(L, (s+1)*k*block_size).
+ * The last non-empty shard may be ragged; trailing shards may be empty (start == end == L).
+ *   seq_lens: host int32[batch], each >= 0 (negative -> DCP_ERR_BAD_PLAN).
+ *   bounds:   host int32[batch][num_shards][2] written as (start, end).
+ * Errors: DCP_ERR_NULL, DCP_ERR_SHAPE (batch < 1, num_shards < 1, block_size < 1),
+ * DCP_ERR_BAD_PLAN. Nothing is written on error.
+ */
+dcp_status dcp_plan_shards(const int32_t* seq_lens, int32_t batch, int32_t num_shards,
+                           int32_t block_size, int32_t* bounds);
+
+/*
+ * dcp_plan_shards_device -- the same plan computed on the device from device seq_lens
+ * (int32[batch]) into device bounds (int32[batch][num_shards][2]). Negative lengths are
+ * treated as 0. Asynchronous on `stream`.
+ */
+dcp_status dcp_plan_shards_device(const int32_t* seq_lens, int32_t batch, int32_t num_shards,
+                                  int32_t block_size, int32_t* bounds, void* stream);
+
+/*
+ * dcp_workspace_bytes -- host only. Size of the workspace that dcp_decode_attn_partial and
+ * dcp_decode_attn need for this shape (the larger, fused, requirement). Allocate it once for
+ * the largest shape in use and pass it to every call. Errors: DCP_ERR_NULL, DCP_ERR_SHAPE,
+ * DCP_ERR_UNSUPPORTED.
+ */
+dcp_status dcp_workspace_bytes(const dcp_attn_shape* shape, size_t* bytes);
+
+/*
+ * dcp_decode_attn_partial -- step 2: per-shard partial attention.
+ *   q:           device [B][Hq][Dqk] (dtype)
+ *   k_cache:     device, GQA [num_blocks][Hkv][block_size][Dqk]; MLA [num_blocks][block_size][Dqk]
+ *   v_cache:     device, GQA same layout as k_cache (Dv == Dqk); MLA must be NULL
+ *   block_table: device int32 [B][max_blocks_per_seq]
+ *   bounds:      device int32 [B][S][2]: shard s of request b covers tokens [start, end).
+ *                Any ranges are accepted (the canonical plan or any other); the merge gives
+ *                the full attention when they partition [0, L_b).
+ *   part_o:      device float [B][S][Hq][Dv]: O_s (softmax output over the shard, fp32)
+ *   part_lse:    device float [B][S][Hq]: LSE_s = ln sum_{t in shard} exp(scale*<q,k_t>);
+ *                an empty shard gives O_s = 0 and LSE_s = -inf.
+ *   workspace:   device, >= dcp_workspace_bytes(); its content need not be initialised
+ *                and is overwritten (do not share one workspace between concurrent calls).
+ * Errors: DCP_ERR_NULL, DCP_ERR_ALIGN, DCP_ERR_SHAPE, DCP_ERR_UNSUPPORTED,
+ * DCP_ERR_WORKSPACE, DCP_ERR_DEVICE.
+ */
+dcp_status dcp_decode_attn_partial(const dcp_attn_shape* shape, const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, const int32_t* bounds,
+                                   float* part_o, float* part_lse, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
+ * dcp_merge_lse -- step 3: combine S partials per (request, head) by LSE re-weighting.
+ *   part_o [B][S][H][Dv], part_lse [B][S][H] (device float) -> out [B][H][Dv] (device float)
+ *   and, if out_lse is not NULL, out_lse [B][H] = the log-sum-exp over the union of shards.
+ * Shards with LSE = -inf contribute nothing; if all are -inf, out = 0 and out_lse = -inf.
+ * Errors: DCP_ERR_NULL, DCP_ERR_ALIGN, DCP_ERR_SHAPE, DCP_ERR_DEVICE.
+ */
+dcp_status dcp_merge_lse(int32_t batch, int32_t num_shards, int32_t num_heads, int32_t head_dim_v,
+                         const float* part_o, const float* part_lse, float* out, float* out_lse,
+                         void* stream);
+
+/*
+ * dcp_decode_attn -- steps 2 and 3 in one call: the per-shard partials are kept in the
+ * workspace (reused every call, step 4) and merged into out [B][Hq][Dv] (device float) and,
+ * if not NULL, out_lse [B][Hq]. Arguments as for dcp_decode_attn_partial.
+ */
+dcp_status dcp_decode_attn(const dcp_attn_shape* shape, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table, const int32_t* bounds,
+                           void* workspace, size_t workspace_bytes, float* out, float* out_lse,
+                           void* stream);
+
+/*
+ * dcp_read_device_flags -- copy the sticky device-side flag word out of a workspace and
+ * wait for `stream`. Bit 0: a bound was clamped into [0, max_blocks_per_seq*block_size] or
+ * had end < start. Bit 1: a block id outside [0, num_blocks) was met and its tokens masked.
+ * Bits are cleared by the next dcp_decode_attn[_partial] call on that workspace.
+ */
+dcp_status dcp_read_device_flags(const void* workspace, int32_t* flags, void* stream);
+
+/*
+ * dcp_debug_gather_shard -- test aid for bit-exact page indexing. Copies the cached rows of
+ * tokens [start, end) of shard (b, s) (bounds read on the device, clamped as above) for KV
+ * head kv_head (GQA; 0 for MLA) from `cache` into dst, row after row, as raw element bits
+ * (head_dim_qk elements per row of the cache's dtype). At most max_rows rows are written.
+ */
+dcp_status dcp_debug_gather_shard(const dcp_attn_shape* shape, const void* cache,
+                                  const int32_t* block_table, const int32_t* bounds, int32_t b,
+                                  int32_t s, int32_t kv_head, void* dst, int32_t max_rows,
+                                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCP_H_ */

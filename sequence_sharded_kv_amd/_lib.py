@@ -1,0 +1,193 @@
+"""ctypes binding of libdcp.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls (include/dcp.h); all the
+work of the path runs in the library's HIP kernels. Device arguments are torch tensors on
+a ROCm device; the call is queued on torch's current stream of that device.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdcp.so")
+
+DCP_OK = 0
+DCP_ERR_NULL = 1
+DCP_ERR_SHAPE = 2
+DCP_ERR_UNSUPPORTED = 3
+DCP_ERR_WORKSPACE = 4
+DCP_ERR_BAD_PLAN = 5
+DCP_ERR_ALIGN = 6
+DCP_ERR_DEVICE = 7
+
+DCP_F32 = 0
+DCP_BF16 = 1
+DCP_KV_GQA = 0
+DCP_KV_MLA = 1
+
+EXPORTS = (
+    "dcp_abi_version", "dcp_status_string", "dcp_last_error", "dcp_plan_shards",
+    "dcp_plan_shards_device", "dcp_workspace_bytes", "dcp_decode_attn_partial", "dcp_merge_lse",
+    "dcp_decode_attn", "dcp_read_device_flags", "dcp_debug_gather_shard",
+)
+
+
+class DcpError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"dcp status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class dcp_attn_shape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim_qk", ctypes.c_int32),
+        ("head_dim_v", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+        ("num_shards", ctypes.c_int32), ("dtype", ctypes.c_int32), ("kv_kind", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdcp.so (built in-tree); raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m sequence_sharded_kv_amd._build`")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    SH = ctypes.POINTER(dcp_attn_shape)
+    sig = {
+        "dcp_abi_version": (I32, []),
+        "dcp_status_string": (ctypes.c_char_p, [I32]),
+        "dcp_last_error": (ctypes.c_char_p, []),
+        "dcp_plan_shards": (I32, [P, I32, I32, I32, P]),
+        "dcp_plan_shards_device": (I32, [P, I32, I32, I32, P, P]),
+        "dcp_workspace_bytes": (I32, [SH, ctypes.POINTER(SZ)]),
+        "dcp_decode_attn_partial": (I32, [SH, P, P, P, P, P, P, P, P, SZ, P]),
+        "dcp_merge_lse": (I32, [I32, I32, I32, I32, P, P, P, P, P]),
+        "dcp_decode_attn": (I32, [SH, P, P, P, P, P, P, SZ, P, P, P]),
+        "dcp_read_device_flags": (I32, [P, ctypes.POINTER(I32), P]),
+        "dcp_debug_gather_shard": (I32, [SH, P, P, P, I32, I32, I32, P, I32, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != DCP_OK:
+        detail = load().dcp_last_error().decode()
+        raise DcpError(status, detail or load().dcp_status_string(status).decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def make_shape(kind: str, dtype: str, batch: int, num_q_heads: int, num_kv_heads: int,
+               head_dim_qk: int, head_dim_v: int, block_size: int, max_blocks_per_seq: int,
+               num_blocks: int, num_shards: int, softmax_scale: float) -> dcp_attn_shape:
+    return dcp_attn_shape(
+        batch, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, block_size,
+        max_blocks_per_seq, num_blocks, num_shards,
+        DCP_BF16 if dtype == "bf16" else DCP_F32 if dtype == "f32" else -1,
+        DCP_KV_MLA if kind == "mla" else DCP_KV_GQA if kind == "gqa" else -1,
+        float(softmax_scale))
+
+
+# ------------------------------------------------------------------ entry points
+
+def dcp_abi_version() -> int:
+    return load().dcp_abi_version()
+
+
+def dcp_status_string(status: int) -> str:
+    return load().dcp_status_string(status).decode()
+
+
+def dcp_last_error() -> str:
+    return load().dcp_last_error().decode()
+
+
+def dcp_plan_shards(seq_lens, num_shards: int, block_size: int) -> np.ndarray:
+    """Host plan: int32 [B, S, 2] of (start, end)."""
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    B = int(lens.shape[0])
+    out = np.zeros((max(B, 1), num_shards if num_shards > 0 else 1, 2), dtype=np.int32)
+    _check(load().dcp_plan_shards(lens.ctypes.data if B else None, B, num_shards, block_size,
+                                  out.ctypes.data))
+    return out
+
+
+def dcp_plan_shards_device(seq_lens, num_shards: int, block_size: int, bounds=None):
+    """Device plan from device int32 seq_lens into device int32 bounds [B, S, 2]."""
+    import torch
+    B = int(seq_lens.shape[0])
+    if bounds is None:
+        bounds = torch.empty((B, num_shards, 2), dtype=torch.int32, device=seq_lens.device)
+    _check(load().dcp_plan_shards_device(_ptr(seq_lens), B, num_shards, block_size, _ptr(bounds),
+                                         _stream(seq_lens)))
+    return bounds
+
+
+def dcp_workspace_bytes(shape: dcp_attn_shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().dcp_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)))
+    return int(n.value)
+
+
+def dcp_decode_attn_partial(shape: dcp_attn_shape, q, k_cache, v_cache, block_table, bounds,
+                            part_o, part_lse, workspace) -> None:
+    _check(load().dcp_decode_attn_partial(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(bounds), _ptr(part_o), _ptr(part_lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q)))
+
+
+def dcp_merge_lse(part_o, part_lse, out, out_lse=None) -> None:
+    B, S, H, Dv = (int(x) for x in part_o.shape)
+    _check(load().dcp_merge_lse(B, S, H, Dv, _ptr(part_o), _ptr(part_lse), _ptr(out),
+                                _ptr(out_lse), _stream(part_o)))
+
+
+def dcp_decode_attn(shape: dcp_attn_shape, q, k_cache, v_cache, block_table, bounds, workspace,
+                    out, out_lse=None) -> None:
+    _check(load().dcp_decode_attn(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(bounds), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+        _ptr(out_lse), _stream(q)))
+
+
+def dcp_read_device_flags(workspace) -> int:
+    v = ctypes.c_int32(0)
+    _check(load().dcp_read_device_flags(_ptr(workspace), ctypes.byref(v), _stream(workspace)))
+    return int(v.value)
+
+
+def dcp_debug_gather_shard(shape: dcp_attn_shape, cache, block_table, bounds, b: int, s: int,
+                           kv_head: int, dst) -> None:
+    row_elems = shape.head_dim_qk
+    max_rows = dst.numel() // row_elems
+    _check(load().dcp_debug_gather_shard(
+        ctypes.byref(shape), _ptr(cache), _ptr(block_table), _ptr(bounds), b, s, kv_head,
+        _ptr(dst), max_rows, _stream(cache)))

@@ -1,0 +1,90 @@
+// Internal declarations shared by the host dispatcher and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dcp.h"
+
+namespace dcp {
+
+// Head region of the workspace: the flag word, then a row of zeros.
+constexpr size_t kWsHeadBytes = 4096;
+constexpr size_t kWsZeroOffset = 256;
+constexpr int32_t kWsZeroWords = 512;  // 2 KB of zeros
+
+// Flag bits in the workspace's sticky device flag word.
+constexpr int32_t kFlagBoundClamped = 1;
+constexpr int32_t kFlagBadBlock = 2;
+
+// Work is split stream-K style: every (unit, page) pair is one page of work, the pages of
+// all units are concatenated in unit order, and worker w takes the contiguous range
+// [w*T/P, (w+1)*T/P). A unit is (request, shard) for MLA and (request, shard, kv head) for
+// GQA. A unit cut by a worker boundary yields pieces (partials over sub-ranges) that a
+// finishing pass merges into the unit's partial.
+//
+// Workspace layout (offsets 256-byte aligned):
+//   flags      int32[64]  sticky device flag word at [0], then a 2 KB zero row at byte 256
+//                         (read in place of a page whose block id is invalid)
+//   pre        int32[U + 1]      exclusive prefix sum of unit page counts, pre[U] = T
+//   ubounds    int32[B*S*2]      sanitised (start, end) per (request, shard)
+//   piece_o    float[2*Pmax][Hu][Dv]
+//   piece_lse  float[2*Pmax][Hu]
+//   part_o     float[B][S][Hq][Dv]   (fused path only)
+//   part_lse   float[B][S][Hq]
+struct WsLayout {
+  size_t flags, pre, ubounds, piece_o, piece_lse, part_o, part_lse, total;
+};
+
+enum class Kernel { kNone = 0, kGqaValu, kGqaMfma, kMlaMfma };
+
+struct Plan {          // host-side decisions for one shape
+  Kernel kernel;
+  int32_t units;       // U
+  int32_t heads_per_unit;  // Hu
+  int32_t max_workers;     // Pmax
+  WsLayout ws;
+};
+
+// Parameters of the partial-attention kernels (passed by value).
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_table;
+  const int32_t* ubounds;   // [B*S][2]
+  const int32_t* pre;       // [U + 1]
+  float* part_o;            // [B][S][Hq][Dv]
+  float* part_lse;          // [B][S][Hq]
+  float* piece_o;           // [2P][Hu][Dv]
+  float* piece_lse;         // [2P][Hu]
+  int32_t* flags;
+  const char* zero_row;     // kWsZeroWords*4 bytes of zeros in the workspace
+  int32_t B, S, Hq, Hkv, G, Dqk, Dv, bs, max_blocks, num_blocks, U, P;
+  float scale_log2;         // softmax_scale * log2(e)
+};
+
+// Launchers (each returns the hipError_t of its launch).
+hipError_t launch_plan_device(const int32_t* seq_lens, int32_t B, int32_t S, int32_t bs,
+                              int32_t* bounds, hipStream_t stream);
+hipError_t launch_schedule(const int32_t* bounds, int32_t B, int32_t S, int32_t units_per_bs,
+                           int32_t bs, int32_t max_blocks, int32_t* ubounds, int32_t* pre,
+                           int32_t* flags, hipStream_t stream);
+hipError_t launch_finish_units(const AttnArgs& a, int32_t Hu, hipStream_t stream);
+hipError_t launch_merge(int32_t B, int32_t S, int32_t H, int32_t Dv, const float* part_o,
+                        const float* part_lse, float* out, float* out_lse, hipStream_t stream);
+hipError_t launch_debug_gather(const dcp_attn_shape& sh, const void* cache,
+                               const int32_t* block_table, const int32_t* bounds, int32_t b,
+                               int32_t s, int32_t kv_head, void* dst, int32_t max_rows,
+                               hipStream_t stream);
+
+// Partial-attention kernels. `workers` returns the P the launcher will use (<= max_workers).
+int32_t gqa_valu_workers(int device, int32_t max_workers);
+hipError_t launch_gqa_valu(const AttnArgs& a, int32_t dtype, hipStream_t stream);
+int32_t gqa_mfma_workers(int device, int32_t Dqk, int32_t max_workers);
+hipError_t launch_gqa_mfma(const AttnArgs& a, hipStream_t stream);
+int32_t mla_mfma_workers(int device, int32_t Hq, int32_t max_workers);
+hipError_t launch_mla_mfma(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace dcp

@@ -1,0 +1,275 @@
+// MLA partial attention with bf16 MFMA: every query head of a request shares one latent KV
+// row per token (576 = 512 latent + 64 rope dims; the value is the first 512 dims).
+//
+// A workgroup is one stream-K worker and holds all query heads of a request, so every KV
+// byte is read from HBM exactly once. Each wave owns 16 heads. Per 32-token tile:
+//   - the tile (32 rows x 1152 B) is copied HBM -> LDS with global_load_lds_dwordx4 (no
+//     register staging), double-buffered so the next tile streams in while this one is used;
+//   - S^T[16 tok x 16 heads] = K[16 x 576] . Q^T[576 x 16] for the two 16-row subtiles
+//     (2 x 18 v_mfma_f32_16x16x32_bf16; K rows from LDS as the A operand, the wave's Q slice
+//     resident in registers as B);
+//   - online softmax per head: a lane holds 8 scores of one head, two shuffles reach the
+//     other three lanes of that head;
+//   - O^T[512 x 16] += V^T[512 x 32] . P^T[32 x 16]  (32 M tiles; V = the first 512 dims of
+//     the same LDS tile, read transposed with ds_read_b64_tr_b16; P from registers, split
+//     into a bf16 high part and a bf16 remainder, two MFMAs).
+//
+// LDS tile layout (36.5 KB): region A = dims 0..511 of the 32 rows, one 1 KB row per DMA
+// instruction, rows padded to 1040 B; region B = dims 512..575, 128 B per row with the 16-byte
+// chunks XOR-swizzled by row. MFMA row m of a 16-row subtile is token pi(m), where
+// pi(8c + 4h + e) = 8c + h + 2e: the K reads of 8 consecutive MFMA rows then touch 8
+// different 16-byte bank groups, and each transposed V read (4 MFMA rows e = 0..3) reads
+// rows 2 apart, whose 32-byte pieces tile 128 bytes of banks without overlap.
+#include "device_common.h"
+
+namespace dcp {
+
+constexpr int kMlaDqk = 576;
+constexpr int kMlaDv = 512;
+constexpr int kMlaTile = 32;
+constexpr int kMlaRowA = 1040;                    // LDS bytes per row, region A (dims 0..511)
+constexpr int kMlaRowB = 128;                     // LDS bytes per row, region B (dims 512..575)
+constexpr int kMlaRegionB = kMlaTile * kMlaRowA;  // offset of region B
+constexpr int kMlaTileBytes = kMlaRegionB + kMlaTile * kMlaRowB;
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Token (within a 16-row subtile) held by MFMA row m (see the layout note above).
+__device__ __forceinline__ int tok_of_row(int m) {
+  return (m & 8) | ((m >> 2) & 1) | ((m & 3) << 1);
+}
+__device__ __forceinline__ int swz_b(int r) { return r & 7; }
+
+__device__ __forceinline__ bf16x8 mla_tr_pair(const char* lo, const char* hi) {
+  i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)lo);
+  i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)hi);
+  typedef __attribute__((ext_vector_type(8))) short i16x8;
+  i16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src, 64);
+  uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+  uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int NW>  // waves per workgroup; 16 heads per wave, Hq = 16 * NW
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
+  __shared__ __attribute__((aligned(1024))) char lds[2][kMlaTileBytes];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int n = lane & 15;        // head within the wave; also the MFMA row this lane loads
+  const int gq = lane >> 4;       // lane quarter (k-slice of the operand layouts)
+  const int32_t w = blockIdx.x;
+  if (w >= a.P) return;
+  const uint16_t* __restrict__ Q = (const uint16_t*)a.q;
+  const char* __restrict__ Kc = (const char*)a.k;
+  const int64_t T_pages = a.pre[a.U];
+  const int64_t g0 = worker_begin(T_pages, a.P, w), g1 = worker_begin(T_pages, a.P, w + 1);
+  if (g0 >= g1) return;
+  int32_t u = find_unit(a.pre, a.U, g0);
+  int64_t g = g0;
+  int32_t bad = 0;
+
+  // per-lane LDS offsets (bytes) within a tile buffer
+  const int krow0 = tok_of_row(n);                  // K row read for MFMA row n, subtile 0
+  const int ka_off = krow0 * kMlaRowA + 16 * gq;    // region A, + 64 j (+ 16 rows for subtile 1)
+  const int vrow = tok_of_row(4 * gq + (n >> 2));   // V row of this lane's transposed read
+  const int v_off = vrow * kMlaRowA + 8 * (n & 3);  // + 32 mt (+ 16 rows for subtile 1)
+
+  while (g < g1) {
+    while ((int64_t)a.pre[u + 1] <= g) ++u;
+    const int64_t up0 = a.pre[u], up1 = a.pre[u + 1];
+    const int64_t sg1 = up1 < g1 ? up1 : g1;
+    const int32_t bsi = u;               // one unit per (request, shard)
+    const int32_t b = bsi / a.S;
+    const int64_t ta = a.ubounds[2 * bsi], te = a.ubounds[2 * bsi + 1];
+    const int64_t pa = ta / a.bs;
+    int64_t t0 = (pa + (g - up0)) * a.bs, t1 = (pa + (sg1 - up0)) * a.bs;
+    if (t0 < ta) t0 = ta;
+    if (t1 > te) t1 = te;
+    const bool whole = (g == up0) && (sg1 == up1);
+    const bool first = (g == g0);
+    const int32_t* brow = a.block_table + (int64_t)b * a.max_blocks;
+
+    // Queue the copy of tile [tile, tile + 32) into buffer `buf`; returns the valid-token mask.
+    auto issue_tile = [&](int64_t tile, int buf) -> uint32_t {
+      uint64_t rowaddr = (uint64_t)zero_row;
+      bool valid = false;
+      if (lane < kMlaTile) {
+        int64_t t = tile + lane;
+        int64_t tc = t < t1 ? t : t1 - 1;
+        int32_t blk = brow[tc / a.bs];
+        bool page_ok = blk >= 0 && blk < a.num_blocks;
+        if (page_ok)
+          rowaddr = (uint64_t)(Kc + ((int64_t)blk * a.bs + tc % a.bs) * (kMlaDqk * 2));
+        else
+          bad = 1;
+        valid = page_ok && t < t1;
+      }
+      const uint32_t mask = (uint32_t)__ballot(valid);
+      char* base = &lds[buf][0];
+      for (int r = wv; r < kMlaTile; r += NW) {
+        const char* src = (const char*)readlane_u64(rowaddr, r) + 16 * lane;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(base + r * kMlaRowA), 16,
+                                         0, 0);
+      }
+      for (int kk = wv; kk < 4; kk += NW) {
+        const int r = 8 * kk + (lane >> 3);
+        const uint64_t ra = shfl_u64(rowaddr, r);
+        const char* src = (const char*)ra + 1024 + 16 * ((lane & 7) ^ swz_b(r));
+        __builtin_amdgcn_global_load_lds((const void*)src,
+                                         (lds_void_t*)(base + kMlaRegionB + kk * 1024), 16, 0, 0);
+      }
+      return mask;
+    };
+
+    // the wave's Q slice as the B operand: lane holds q[16wv + n][32j + 8gq .. +8]
+    bf16x8 qop[kMlaDqk / 32];
+    {
+      const uint16_t* qrow = Q + ((int64_t)b * a.Hq + 16 * wv + n) * kMlaDqk + 8 * gq;
+#pragma unroll
+      for (int j = 0; j < kMlaDqk / 32; ++j)
+        qop[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 32 * j));
+    }
+
+    f32x4 acc[kMlaDv / 16];
+#pragma unroll
+    for (int i = 0; i < kMlaDv / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = kNegInf, l_run = 0.f;
+
+    uint32_t mask_next = issue_tile(t0, 0);
+    __syncthreads();
+    int cur = 0;
+    for (int64_t tile = t0; tile < t1; tile += kMlaTile) {
+      const uint32_t mask = mask_next;
+      if (tile + kMlaTile < t1) mask_next = issue_tile(tile + kMlaTile, cur ^ 1);
+      const char* tb = &lds[cur][0];
+
+      // S^T = K . Q^T for the two 16-row subtiles
+      f32x4 s[2];
+#pragma unroll
+      for (int at = 0; at < 2; ++at) {
+        s[at] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int kr = 16 * at + krow0;
+        const char* pa_ = tb + ka_off + at * 16 * kMlaRowA;
+        const char* pb_ = tb + kMlaRegionB + kr * kMlaRowB;
+#pragma unroll
+        for (int j = 0; j < kMlaDqk / 32; ++j) {
+          const char* p = (j < 16) ? pa_ + 64 * j
+                                   : pb_ + 16 * ((4 * (j - 16) + gq) ^ swz_b(kr));
+          const bf16x8 kop = __builtin_bit_cast(bf16x8, *(const u32x4*)p);
+          s[at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[j], s[at], 0, 0, 0);
+        }
+      }
+
+      // online softmax; s[at][i] is MFMA row 4gq + i of subtile at (token 16at + pi(4gq + i))
+      float x[8];
+      float tmax = kNegInf;
+#pragma unroll
+      for (int at = 0; at < 2; ++at)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 16 * at + tok_of_row(4 * gq + i);
+          const float v = ((mask >> tok) & 1u) ? s[at][i] * a.scale_log2 : kNegInf;
+          x[4 * at + i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+      float psum = 0.f;
+      bf16x8 phi, plo;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float p = (x[k] == kNegInf) ? 0.f : fast_exp2(x[k] - m_new);
+        psum += p;
+        const __bf16 hi = (__bf16)p;
+        phi[k] = hi;
+        plo[k] = (__bf16)(p - (float)hi);
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      if (!__all(alpha == 1.f)) {
+#pragma unroll
+        for (int i = 0; i < kMlaDv / 16; ++i) acc[i] *= alpha;
+      }
+
+      // O^T += V^T . P^T; slots 0..3 are subtile-0 rows 4gq + e, slots 4..7 subtile-1 rows
+      {
+        const char* vb = tb + v_off;
+#pragma unroll
+        for (int mt = 0; mt < kMlaDv / 16; ++mt) {
+          const bf16x8 vop = mla_tr_pair(vb + 32 * mt, vb + 16 * kMlaRowA + 32 * mt);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo, acc[mt], 0, 0, 0);
+        }
+      }
+      __syncthreads();
+      cur ^= 1;
+    }
+
+    // finalise this segment: l over the four lanes of head n
+    float l = l_run;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int head = 16 * wv + n;
+    float* dst_o;
+    float* dst_l;
+    if (whole) {
+      dst_o = a.part_o + ((int64_t)bsi * a.Hq + head) * kMlaDv;
+      dst_l = a.part_lse + (int64_t)bsi * a.Hq + head;
+    } else {
+      const int32_t slot = piece_slot(w, first);
+      dst_o = a.piece_o + ((int64_t)slot * a.Hq + head) * kMlaDv;
+      dst_l = a.piece_lse + (int64_t)slot * a.Hq + head;
+    }
+#pragma unroll
+    for (int mt = 0; mt < kMlaDv / 16; ++mt) *(f32x4*)(dst_o + 16 * mt + 4 * gq) = acc[mt] * inv;
+    if (gq == 0) *dst_l = l > 0.f ? (m_run + fast_log2(l)) * kLn2 : kNegInf;
+    g = sg1;
+  }
+  if (bad) atomicOr(a.flags, kFlagBadBlock);
+}
+
+static int mla_cus(int device) {
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  return cus;
+}
+
+int32_t mla_mfma_workers(int device, int32_t Hq, int32_t max_workers) {
+  // LDS (2 x 36.5 KB per workgroup) allows two resident workgroups per CU; registers allow
+  // two waves per SIMD, so two workgroups fit while a workgroup has at most four waves.
+  const int nw = Hq / 16;
+  const int per_cu = nw <= 4 ? 2 : 1;
+  int32_t p = mla_cus(device) * per_cu;
+  return p < max_workers ? p : max_workers;
+}
+
+hipError_t launch_mla_mfma(const AttnArgs& a, hipStream_t stream) {
+  const char* zr = a.zero_row;
+  switch (a.Hq / 16) {
+    case 1: hipLaunchKernelGGL((mla_mfma_kernel<1>), dim3(a.P), dim3(64), 0, stream, a, zr); break;
+    case 2: hipLaunchKernelGGL((mla_mfma_kernel<2>), dim3(a.P), dim3(128), 0, stream, a, zr); break;
+    case 4: hipLaunchKernelGGL((mla_mfma_kernel<4>), dim3(a.P), dim3(256), 0, stream, a, zr); break;
+    case 8: hipLaunchKernelGGL((mla_mfma_kernel<8>), dim3(a.P), dim3(512), 0, stream, a, zr); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dcp

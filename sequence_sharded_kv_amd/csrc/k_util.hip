@@ -1,0 +1,256 @@
+// Small kernels around the partial-attention kernels: device shard plan, work schedule,
+// per-unit finishing (merging the pieces of units cut by worker boundaries), the LSE merge
+// across shards, and the debug page gather.
+#include "device_common.h"
+
+namespace dcp {
+
+// ---------------------------------------------------------------- device shard plan
+
+// Canonical plan (page-aligned ceil split, see dcp_plan_shards in dcp.h): one thread per
+// (request, shard).
+__global__ void plan_device_kernel(const int32_t* __restrict__ seq_lens, int32_t B, int32_t S,
+                                   int32_t bs, int32_t* __restrict__ bounds) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)B * S) return;
+  int32_t b = (int32_t)(i / S), s = (int32_t)(i % S);
+  int64_t L = seq_lens[b];
+  if (L < 0) L = 0;
+  int64_t pages = (L + bs - 1) / bs;
+  int64_t per = (pages + S - 1) / S;
+  int64_t a = (int64_t)s * per * bs, e = (int64_t)(s + 1) * per * bs;
+  bounds[2 * i] = (int32_t)(a < L ? a : L);
+  bounds[2 * i + 1] = (int32_t)(e < L ? e : L);
+}
+
+hipError_t launch_plan_device(const int32_t* seq_lens, int32_t B, int32_t S, int32_t bs,
+                              int32_t* bounds, hipStream_t stream) {
+  int64_t n = (int64_t)B * S;
+  int32_t grid = (int32_t)((n + 255) / 256);
+  hipLaunchKernelGGL(plan_device_kernel, dim3(grid), dim3(256), 0, stream, seq_lens, B, S, bs,
+                     bounds);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- schedule
+
+// One workgroup: sanitise the bounds of every (request, shard), count each unit's pages and
+// write the exclusive prefix sum pre[0..U] (units ordered (b, s, h) with h < units_per_bs).
+// Also clears the flag word (the first call of a step owns it).
+constexpr int kSchedThreads = 1024;
+
+__global__ void __launch_bounds__(kSchedThreads)
+schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_t units_per_bs,
+                int32_t bs, int32_t max_blocks, int32_t* __restrict__ ubounds,
+                int32_t* __restrict__ pre, int32_t* __restrict__ flags) {
+  __shared__ int32_t warp_sums[kSchedThreads / 64];
+  __shared__ int32_t carry;
+  __shared__ int32_t flag_acc;
+  const int tid = threadIdx.x;
+  if (tid == 0) { carry = 0; flag_acc = 0; }
+  for (int i = tid; i < kWsZeroWords; i += kSchedThreads) flags[kWsZeroOffset / 4 + i] = 0;
+  __syncthreads();
+  const int64_t cap = (int64_t)max_blocks * bs;
+  const int64_t nbs = (int64_t)B * S;
+  const int64_t U = nbs * units_per_bs;
+  int32_t my_flag = 0;
+  for (int64_t base = 0; base < U; base += kSchedThreads) {
+    int64_t u = base + tid;
+    int32_t cnt = 0;
+    if (u < U) {
+      int64_t bsi = u / units_per_bs;
+      int64_t a = bounds[2 * bsi], e = bounds[2 * bsi + 1];
+      int64_t a0 = a, e0 = e;
+      if (a < 0) a = 0;
+      if (e > cap) e = cap;
+      if (a > cap) a = cap;
+      if (e < a) e = a;
+      if (a != a0 || e != e0) my_flag |= kFlagBoundClamped;
+      if (u % units_per_bs == 0) {
+        ubounds[2 * bsi] = (int32_t)a;
+        ubounds[2 * bsi + 1] = (int32_t)e;
+      }
+      cnt = (e > a) ? (int32_t)((e + bs - 1) / bs - a / bs) : 0;
+    }
+    // inclusive scan within the wave
+    int lane = tid & 63, wv = tid >> 6;
+    int32_t x = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int32_t y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) warp_sums[wv] = x;
+    __syncthreads();
+    if (wv == 0) {
+      int32_t ws = (lane < kSchedThreads / 64) ? warp_sums[lane] : 0;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        int32_t y = __shfl_up(ws, off, 64);
+        if (lane >= off) ws += y;
+      }
+      if (lane < kSchedThreads / 64) warp_sums[lane] = ws;  // inclusive over waves
+    }
+    __syncthreads();
+    int32_t excl = carry + (wv > 0 ? warp_sums[wv - 1] : 0) + x - cnt;
+    if (u < U) pre[u] = excl;
+    __syncthreads();
+    if (tid == kSchedThreads - 1) carry = excl + cnt;
+    __syncthreads();
+  }
+  if (my_flag) atomicOr(&flag_acc, my_flag);
+  __syncthreads();
+  if (tid == 0) {
+    pre[U] = carry;
+    flags[0] = flag_acc;
+  }
+}
+
+hipError_t launch_schedule(const int32_t* bounds, int32_t B, int32_t S, int32_t units_per_bs,
+                           int32_t bs, int32_t max_blocks, int32_t* ubounds, int32_t* pre,
+                           int32_t* flags, hipStream_t stream) {
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, bounds, B, S,
+                     units_per_bs, bs, max_blocks, ubounds, pre, flags);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- finish units
+
+// One workgroup per unit. Units with no pages get O = 0, LSE = -inf. Units covered by one
+// worker were written whole by the partial kernel. Units cut by worker boundaries have one
+// piece per covering worker; they are merged here by the LSE formula.
+constexpr int kFinishThreads = 256;
+
+__global__ void __launch_bounds__(kFinishThreads)
+finish_units_kernel(AttnArgs a, int32_t Hu) {
+  const int32_t u = blockIdx.x;
+  const int64_t T = a.pre[a.U];
+  const int64_t p0 = a.pre[u], p1 = a.pre[u + 1];
+  const int32_t bsi = u / (a.U / (a.B * a.S));
+  const int32_t hsub = u % (a.U / (a.B * a.S));
+  float* out_o = a.part_o + ((int64_t)bsi * a.Hq + (int64_t)hsub * Hu) * a.Dv;
+  float* out_l = a.part_lse + (int64_t)bsi * a.Hq + (int64_t)hsub * Hu;
+  const int32_t n = Hu * a.Dv;
+  if (p1 == p0) {
+    for (int32_t i = threadIdx.x; i < n; i += blockDim.x) out_o[i] = 0.f;
+    for (int32_t i = threadIdx.x; i < Hu; i += blockDim.x) out_l[i] = kNegInf;
+    return;
+  }
+  const int32_t w0 = worker_of(T, a.P, p0), w1 = worker_of(T, a.P, p1 - 1);
+  if (w0 == w1) return;
+  // pieces: slot of worker w for this unit
+  for (int32_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const int32_t h = i / a.Dv;
+    float m = kNegInf;
+    for (int32_t w = w0; w <= w1; ++w) {
+      int64_t wb = worker_begin(T, a.P, w);
+      if (worker_begin(T, a.P, w + 1) == wb) continue;
+      int32_t slot = piece_slot(w, !(w == w0 && wb < p0));
+      m = fmaxf(m, a.piece_lse[(int64_t)slot * Hu + h]);
+    }
+    float den = 0.f, acc = 0.f;
+    for (int32_t w = w0; w <= w1; ++w) {
+      int64_t wb = worker_begin(T, a.P, w);
+      if (worker_begin(T, a.P, w + 1) == wb) continue;
+      int32_t slot = piece_slot(w, !(w == w0 && wb < p0));
+      float wt = safe_exp_diff(a.piece_lse[(int64_t)slot * Hu + h], m);
+      den += wt;
+      acc += wt * a.piece_o[(int64_t)slot * n + i];
+    }
+    out_o[i] = den > 0.f ? acc / den : 0.f;
+    if (i % a.Dv == 0) out_l[h] = den > 0.f ? m + logf(den) : kNegInf;
+  }
+}
+
+hipError_t launch_finish_units(const AttnArgs& a, int32_t Hu, hipStream_t stream) {
+  if (a.U == 0) return hipSuccess;
+  hipLaunchKernelGGL(finish_units_kernel, dim3(a.U), dim3(kFinishThreads), 0, stream, a, Hu);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- LSE merge
+
+// out[b, h, :] = sum_s exp(LSE_s - LSE) O_s with LSE = M + ln sum_s exp(LSE_s - M).
+// One thread per 4 output values; a workgroup covers 256 x 4 values of one or more heads.
+__global__ void __launch_bounds__(256)
+merge_kernel(int32_t B, int32_t S, int32_t H, int32_t Dv, const float* __restrict__ part_o,
+             const float* __restrict__ part_lse, float* __restrict__ out,
+             float* __restrict__ out_lse) {
+  const int64_t q4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // float4 index
+  const int32_t dv4 = Dv >> 2;
+  if (q4 >= (int64_t)B * H * dv4) return;
+  const int64_t bh = q4 / dv4;
+  const int32_t c = (int32_t)(q4 % dv4);
+  const int64_t b = bh / H, h = bh % H;
+  const float* lse = part_lse + b * S * H + h;
+  float m = kNegInf;
+  for (int32_t s = 0; s < S; ++s) m = fmaxf(m, lse[(int64_t)s * H]);
+  float den = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int32_t s = 0; s < S; ++s) {
+    float w = safe_exp_diff(lse[(int64_t)s * H], m);
+    den += w;
+    if (w != 0.f) {
+      const f32x4 o = *(const f32x4*)(part_o + ((b * S + s) * H + h) * Dv + 4 * c);
+      acc += w * o;
+    }
+  }
+  float inv = den > 0.f ? 1.f / den : 0.f;
+  *(f32x4*)(out + bh * Dv + 4 * c) = acc * inv;
+  if (out_lse && c == 0) out_lse[bh] = den > 0.f ? m + logf(den) : kNegInf;
+}
+
+hipError_t launch_merge(int32_t B, int32_t S, int32_t H, int32_t Dv, const float* part_o,
+                        const float* part_lse, float* out, float* out_lse, hipStream_t stream) {
+  int64_t n = (int64_t)B * H * (Dv / 4);
+  int32_t grid = (int32_t)((n + 255) / 256);
+  hipLaunchKernelGGL(merge_kernel, dim3(grid), dim3(256), 0, stream, B, S, H, Dv, part_o,
+                     part_lse, out, out_lse);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- debug gather
+
+__global__ void debug_gather_kernel(const uint8_t* __restrict__ cache,
+                                    const int32_t* __restrict__ block_table,
+                                    const int32_t* __restrict__ bounds, int32_t S, int32_t b,
+                                    int32_t s, int32_t kv_head, int32_t Hkv, int32_t bs,
+                                    int32_t max_blocks, int32_t num_blocks, int32_t row_bytes,
+                                    int32_t gqa, uint8_t* __restrict__ dst, int32_t max_rows) {
+  int64_t cap = (int64_t)max_blocks * bs;
+  int64_t a = bounds[2 * ((int64_t)b * S + s)], e = bounds[2 * ((int64_t)b * S + s) + 1];
+  if (a < 0) a = 0;
+  if (e > cap) e = cap;
+  if (a > cap) a = cap;
+  if (e < a) e = a;
+  int64_t n = e - a;
+  if (n > max_rows) n = max_rows;
+  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
+    int64_t t = a + r;
+    int32_t blk = block_table[(int64_t)b * max_blocks + t / bs];
+    int32_t slot = (int32_t)(t % bs);
+    uint8_t* d = dst + r * row_bytes;
+    if (blk < 0 || blk >= num_blocks) {
+      for (int32_t i = threadIdx.x; i < row_bytes; i += blockDim.x) d[i] = 0;
+      continue;
+    }
+    int64_t row = gqa ? (((int64_t)blk * Hkv + kv_head) * bs + slot) : ((int64_t)blk * bs + slot);
+    const uint8_t* src = cache + row * row_bytes;
+    for (int32_t i = threadIdx.x; i < row_bytes; i += blockDim.x) d[i] = src[i];
+  }
+}
+
+hipError_t launch_debug_gather(const dcp_attn_shape& sh, const void* cache,
+                               const int32_t* block_table, const int32_t* bounds, int32_t b,
+                               int32_t s, int32_t kv_head, void* dst, int32_t max_rows,
+                               hipStream_t stream) {
+  int32_t esize = sh.dtype == DCP_F32 ? 4 : 2;
+  int32_t row_bytes = sh.head_dim_qk * esize;
+  hipLaunchKernelGGL(debug_gather_kernel, dim3(256), dim3(256), 0, stream,
+                     (const uint8_t*)cache, block_table, bounds, sh.num_shards, b, s, kv_head,
+                     sh.num_kv_heads, sh.block_size, sh.max_blocks_per_seq, sh.num_blocks,
+                     row_bytes, sh.kv_kind == DCP_KV_GQA ? 1 : 0, (uint8_t*)dst, max_rows);
+  return hipGetLastError();
+}
+
+}  // namespace dcp

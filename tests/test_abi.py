@@ -1,0 +1,156 @@
+"""The C ABI without a GPU: exports, version, status strings, host plan and every
+host-checked error path (each must return before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sequence_sharded_kv_amd as dcp
+from oracle import plan_shards as oracle_plan
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "dcp.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dcp_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = dcp.load()
+    names = declared_functions()
+    assert len(names) == 11, names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert sorted(dcp.EXPORTS) == names
+
+
+def test_version_and_status_strings():
+    assert dcp.dcp_abi_version() == 1
+    for s in range(8):
+        assert dcp.dcp_status_string(s)
+    assert dcp.dcp_status_string(99) == "unknown status"
+
+
+def test_host_plan_matches_oracle_bit_exact():
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        B = int(rng.integers(1, 9))
+        S = int(rng.integers(1, 33))
+        bs = int(rng.choice([1, 16, 64]))
+        lens = rng.integers(0, 300_000, size=B).astype(np.int32)
+        lens[rng.random(B) < 0.2] = rng.integers(0, 3)
+        got = dcp.dcp_plan_shards(lens, S, bs)
+        want = oracle_plan(lens.tolist(), S, bs)
+        assert got.dtype == np.int32 and np.array_equal(got.astype(np.int64), want)
+
+
+def test_host_plan_pages_example():
+    got = dcp.dcp_plan_shards([200_000, 1_000_000], 4, 16)
+    assert got[0].tolist() == [[0, 50_000], [50_000, 100_000], [100_000, 150_000],
+                               [150_000, 200_000]]
+    got = dcp.dcp_plan_shards([1_000_000], 16, 16)
+    assert got[0, -1].tolist() == [937_680, 1_000_000]
+    assert (got[0, :, 1] - got[0, :, 0]).tolist() == [62_512] * 15 + [62_320]
+
+
+@pytest.mark.parametrize("args,code", [
+    (([5], 0, 16), dcp.DCP_ERR_SHAPE),
+    (([5], 4, 0), dcp.DCP_ERR_SHAPE),
+    (([5, -1], 4, 16), dcp.DCP_ERR_BAD_PLAN),
+])
+def test_host_plan_errors(args, code):
+    with pytest.raises(dcp.DcpError) as e:
+        dcp.dcp_plan_shards(*args)
+    assert e.value.status == code
+
+
+def _shape(**kw):
+    base = dict(kind="mla", dtype="bf16", batch=4, num_q_heads=64, num_kv_heads=1, head_dim_qk=576,
+                head_dim_v=512, block_size=64, max_blocks_per_seq=16, num_blocks=64, num_shards=8,
+                softmax_scale=192 ** -0.5)
+    base.update(kw)
+    return dcp.make_shape(**base)
+
+
+def test_workspace_bytes_and_shape_errors():
+    n = dcp.dcp_workspace_bytes(_shape())
+    assert n > 4 * 8 * 64 * 512 * 4
+    assert n % 256 == 0
+    bad = [
+        dict(batch=0), dict(num_shards=0), dict(block_size=0), dict(num_q_heads=60, num_kv_heads=8),
+        dict(kind="gqa", head_dim_v=64), dict(num_kv_heads=2, num_q_heads=64),
+        dict(dtype="fp8"), dict(kind="xyz"), dict(softmax_scale=float("inf")),
+        dict(head_dim_v=510, head_dim_qk=576),
+    ]
+    for kw in bad:
+        with pytest.raises(dcp.DcpError) as e:
+            dcp.dcp_workspace_bytes(_shape(**kw))
+        assert e.value.status == dcp.DCP_ERR_SHAPE, kw
+    unsupported = [dict(num_q_heads=48), dict(dtype="f32"), dict(head_dim_qk=320, head_dim_v=256),
+                   dict(kind="gqa", num_q_heads=64, num_kv_heads=2, head_dim_qk=128,
+                        head_dim_v=128)]
+    for kw in unsupported:
+        with pytest.raises(dcp.DcpError) as e:
+            dcp.dcp_workspace_bytes(_shape(**kw))
+        assert e.value.status == dcp.DCP_ERR_UNSUPPORTED, kw
+
+
+class _Fake:
+    """Stands in for a device tensor: only its address is used before validation fails."""
+
+    def __init__(self, addr, nbytes=1 << 20):
+        self.addr, self.nbytes = addr, nbytes
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.nbytes
+
+    def element_size(self):
+        return 1
+
+
+def _call_partial(sh, q, k, v, bt, bounds, po, pl, ws):
+    lib = dcp.load()
+    p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    return lib.dcp_decode_attn_partial(ctypes.byref(sh), p(q), p(k), p(v), p(bt), p(bounds),
+                                       p(po), p(pl), p(ws), ws.nbytes if ws else 0, None)
+
+
+def test_partial_error_paths_return_before_device_work():
+    sh = _shape()
+    need = dcp.dcp_workspace_bytes(sh)
+    A = lambda: _Fake(0x10000)  # noqa: E731
+    ws_ok = _Fake(0x20000, need)
+    assert _call_partial(sh, None, A(), None, A(), A(), A(), A(), ws_ok) == dcp.DCP_ERR_NULL
+    assert _call_partial(sh, A(), A(), A(), A(), A(), A(), A(), ws_ok) == dcp.DCP_ERR_SHAPE
+    assert _call_partial(sh, _Fake(0x10008), A(), None, A(), A(), A(), A(), ws_ok) == \
+        dcp.DCP_ERR_ALIGN
+    assert _call_partial(sh, A(), A(), None, A(), A(), A(), A(), _Fake(0x20000, need - 1)) == \
+        dcp.DCP_ERR_WORKSPACE
+    gqa = _shape(kind="gqa", num_q_heads=8, num_kv_heads=2, head_dim_qk=64, head_dim_v=64)
+    assert _call_partial(gqa, A(), A(), None, A(), A(), A(), A(), ws_ok) == dcp.DCP_ERR_NULL
+    assert "v_cache" in dcp.dcp_last_error()
+
+
+def test_merge_and_fused_error_paths():
+    lib = dcp.load()
+    assert lib.dcp_merge_lse(2, 4, 8, 64, None, 0x1000, 0x2000, None, None) == dcp.DCP_ERR_NULL
+    assert lib.dcp_merge_lse(2, 4, 8, 62, 0x1000, 0x1000, 0x2000, None, None) == dcp.DCP_ERR_SHAPE
+    assert lib.dcp_merge_lse(0, 4, 8, 64, 0x1000, 0x1000, 0x2000, None, None) == dcp.DCP_ERR_SHAPE
+    assert lib.dcp_merge_lse(2, 4, 8, 64, 0x1004, 0x1000, 0x2000, None, None) == dcp.DCP_ERR_ALIGN
+    sh = _shape()
+    assert lib.dcp_decode_attn(ctypes.byref(sh), 0x1000, 0x1000, None, 0x1000, 0x1000, 0x1000, 16,
+                               None, None, None) == dcp.DCP_ERR_NULL
+    assert lib.dcp_decode_attn(ctypes.byref(sh), 0x1000, 0x1000, None, 0x1000, 0x1000, 0x1000, 16,
+                               0x3000, None, None) == dcp.DCP_ERR_WORKSPACE
+    assert lib.dcp_debug_gather_shard(ctypes.byref(sh), 0x1000, 0x1000, 0x1000, 9, 0, 0, 0x1000, 4,
+                                      None) == dcp.DCP_ERR_SHAPE
+    assert lib.dcp_read_device_flags(None, None, None) == dcp.DCP_ERR_NULL
