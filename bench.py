@@ -1,0 +1,309 @@
+#!/usr/bin/env python
+"""Benchmark of sequence-sharded paged decode attention + LSE merge on one MI355X.
+
+One step = one dcp_decode_attn call (per-shard partials over the paged KV cache, kept in the
+reused workspace, then the LSE merge) for the whole batch of one layer, with Q and the KV
+cache already resident in HBM. The default workload is the agent-style MLA decode batch:
+512 requests, 64 query heads sharing one 576-dim latent (value = first 512 dims), bf16,
+lognormal contexts with median 67K tokens, 64-token pages, 8 contiguous shards per request.
+
+Prints one JSON line: the whole-step algorithmic HBM throughput (TB/s) as `value`, decode
+steps/s, the dominant kernel's roofline (its own launch time from HIP events recorded by
+the library on the launch stream) and the float64 CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "mla": ["k_mla_mfma.hip", "device_common.h", "dcp_internal.h"],
+    "gqa-mfma": ["k_gqa_mfma.hip", "device_common.h", "dcp_internal.h"],
+    "gqa-valu": ["k_gqa_valu.hip", "device_common.h", "dcp_internal.h"],
+}
+KERNEL_NAMES = {"mla": "mla_mfma_kernel", "gqa-mfma": "gqa_mfma_kernel",
+                "gqa-valu": "gqa_valu_kernel"}
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="mla-64h-b512")
+    p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle sample")
+    p.add_argument("--calibration-copy-gib", type=float, default=0.0,
+                   help="before timing, run one fp32 x1.0 elementwise pass over this many GiB "
+                        "(reference dispatch for counter calibration)")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                        "script and print the traffic JSON")
+    p.add_argument("--pmc-calibration-gib", type=float, default=1.0)
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ byte model
+
+def kernel_family(wl):
+    if wl.kind == "mla":
+        return "mla"
+    g = wl.num_q_heads // wl.num_kv_heads
+    if wl.dtype == "bf16" and g <= 16 and wl.head_dim_qk in (64, 128):
+        return "gqa-mfma"
+    return "gqa-valu"
+
+
+def byte_model(wl, lens):
+    """Algorithmic bytes of one step: what the method must move at least once."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    tokens = int(np.sum(lens))
+    if wl.kind == "mla":
+        kv = tokens * wl.head_dim_qk * esz                      # V shares the latent bytes
+    else:
+        kv = tokens * wl.num_kv_heads * wl.head_dim_qk * esz * 2
+    q = wl.batch * wl.num_q_heads * wl.head_dim_qk * esz
+    table = int(np.sum(-(-np.asarray(lens, np.int64) // wl.block_size))) * 4
+    part = wl.batch * wl.num_shards * wl.num_q_heads * (wl.head_dim_v + 1) * 4
+    out = wl.batch * wl.num_q_heads * (wl.head_dim_v + 1) * 4
+    return {"kv": kv, "q": q, "table": table, "partials_rw": 2 * part, "out": out,
+            "step": kv + q + table + 2 * part + out,
+            "partial_kernel": kv + q + table + part, "tokens": tokens}
+
+
+def sources_sha(family):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[family]:
+        with open(os.path.join(ROOT, "sequence_sharded_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_file(workload):
+    return os.path.join(PROFILES, f"traffic_{workload}.json")
+
+
+def load_traffic(workload, family):
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_sources_sha256") != sources_sha(family):
+        return None  # the kernel changed since the counters were taken
+    return t
+
+
+# ------------------------------------------------------------------ rocprofv3 counters
+
+def _read_counter_csv(d, counter):
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((int(r.get("Dispatch_Id", 0)), r.get("Kernel_Name", ""),
+                                 float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, family, calib_gib):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant kernel, scaled by what the
+    same counters read for the fp32 elementwise reference pass over calib_gib GiB."""
+    out = {"workload": workload, "kernel": KERNEL_NAMES[family],
+           "kernel_sources_sha256": sources_sha(family)}
+    ref_bytes = calib_gib * (1 << 30)
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _read_counter_csv(d, name)
+        ker = [v for _, k, v in rows if KERNEL_NAMES[family] in k]
+        ref = [v for _, k, v in rows if "elementwise" in k.lower() and v * 1024 > 0.5 * ref_bytes]
+        if not ker or not ref:
+            raise SystemExit(f"{name}: no dispatches of {KERNEL_NAMES[family]} or of the reference "
+                             f"pass in {d}")
+        scale = ref_bytes / (ref[0] * 1024.0)
+        out[name.lower() + "_kib_raw_mean"] = float(np.mean(ker))
+        out[name.lower() + "_calibration_scale"] = scale
+        out[name.lower() + "_bytes_per_launch"] = float(np.mean(ker)) * 1024.0 * scale
+        out[name.lower() + "_dispatches"] = len(ker)
+    out["traffic_bytes_per_launch"] = out["fetch_size_bytes_per_launch"] + \
+        out["write_size_bytes_per_launch"]
+    return out
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(wl, inp, bounds_np, seconds):
+    """The float64 oracle, as it stands, on whole sequences drawn in a seeded order until
+    about `seconds` of CPU time; throughput in the GPU value's unit (TB/s of the step's
+    algorithmic bytes, scaled to the sample)."""
+    import torch
+    from oracle import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    lens = inp["seq_lens_host"]
+    bt = inp["block_table_host"]
+    order = np.random.default_rng(7).permutation(wl.batch)
+    names = ("kv_cache",) if wl.kind == "mla" else ("k_cache", "v_cache")
+
+    def host(t):
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    q_all = host(inp["q"])
+    elapsed, done = 0.0, []
+    for b in order:
+        b = int(b)
+        n = -(-int(lens[b]) // wl.block_size)
+        idx = torch.from_numpy(bt[b, :n].astype(np.int64)).to(inp["q"].device)
+        caches = tuple(host(inp[nm].index_select(0, idx)) for nm in names)
+        table = np.arange(max(n, 1), dtype=np.int32)[None, :]
+        t0 = time.perf_counter()
+        po, pl = O.partial_attention(wl.kind, wl.dtype, q_all[b:b + 1], caches, table,
+                                     bounds_np[b:b + 1].astype(np.int64), wl.block_size,
+                                     wl.softmax_scale, wl.head_dim_v)
+        O.merge_lse(po, pl)
+        elapsed += time.perf_counter() - t0
+        done.append(b)
+        if elapsed >= seconds:
+            break
+    sample = byte_model(wl.replace(batch=len(done)), lens[done])
+    return {"value": sample["step"] / elapsed / 1e12, "unit": "TB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(done)} of {wl.batch} requests ({sample['tokens']} tokens, all "
+                      f"{wl.num_shards} shards + merge), float64 numpy, {elapsed:.1f} s"}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse_args()
+    from workloads import make_device_inputs, workload
+    wl = workload(args.workload)
+    family = kernel_family(wl)
+    if args.summarize_pmc:
+        print(json.dumps(summarize_pmc(*args.summarize_pmc, args.workload, family,
+                                       args.pmc_calibration_gib), indent=1))
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build runs every shard on one device and issues "
+              f"no collectives (asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
+              file=sys.stderr)
+        return 2
+    import torch
+    import sequence_sharded_kv_amd as dcp
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    inp = make_device_inputs(wl, dev, seed=args.seed)
+    lens = inp["seq_lens_host"]
+    bounds_np = dcp.dcp_plan_shards(lens, wl.num_shards, wl.block_size)
+    bounds = torch.from_numpy(bounds_np).to(dev)
+    sh = dcp.make_shape(wl.kind, wl.dtype, wl.batch, wl.num_q_heads, wl.num_kv_heads,
+                        wl.head_dim_qk, wl.head_dim_v, wl.block_size,
+                        int(inp["block_table_host"].shape[1]), int(inp["num_blocks"]),
+                        wl.num_shards, wl.softmax_scale)
+    ws = dcp.alloc_workspace(sh, dev)
+    out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim_v), dtype=torch.float32, device=dev)
+    out_lse = torch.empty((wl.batch, wl.num_q_heads), dtype=torch.float32, device=dev)
+    k_cache = inp["kv_cache"] if wl.kind == "mla" else inp["k_cache"]
+    v_cache = None if wl.kind == "mla" else inp["v_cache"]
+    torch.cuda.synchronize()
+    print(f"[bench] {wl.name}: inputs ready in {time.perf_counter() - t_gen:.1f} s, "
+          f"{int(lens.sum())} tokens", file=sys.stderr, flush=True)
+
+    def step():
+        dcp.dcp_decode_attn(sh, inp["q"], k_cache, v_cache, inp["block_table"], bounds, ws, out,
+                            out_lse)
+
+    if args.calibration_copy_gib > 0:
+        n = int(args.calibration_copy_gib * (1 << 30) // 4)
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        del a, b
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert dcp.dcp_read_device_flags(ws) == 0
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    dcp.dcp_kernel_timing_begin(K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record()
+        step()
+        ends[i].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    launches, kernel_ms = dcp.dcp_kernel_timing_end()
+    per_step = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    ms_per_step = (t1 - t0) * 1e3 / K
+    bm = byte_model(wl, lens)
+    value = bm["step"] / (ms_per_step * 1e-3) / 1e12
+    kern_avg_ms = kernel_ms / max(launches, 1)
+    achieved = bm["partial_kernel"] / (kern_avg_ms * 1e-3) / 1e9
+    traffic = load_traffic(wl.name, family)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else int(traffic["traffic_bytes_per_launch"]),
+                "kernel": KERNEL_NAMES[family], "kernel_avg_ms": round(kern_avg_ms, 4),
+                "algorithmic_bytes_per_launch": int(bm["partial_kernel"])}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, inp, bounds_np, args.cpu_seconds)
+    q = np.percentile(per_step, [10, 50, 90])
+    line = {
+        "metric": "sharded decode-attn achieved HBM TB/s (% peak) + decode steps/s, MLA 67K ctx"
+        if wl.kind == "mla" else "sharded decode-attn achieved HBM TB/s (% peak) + decode steps/s",
+        "value": round(value, 4), "unit": "TB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "steps_per_s": round(1e3 / ms_per_step, 2),
+        "pct_of_hbm_peak": round(100 * value * 1e3 / HBM_PEAK_GBS, 2),
+        "ms_per_step_p10_p50_p90": [round(float(x), 4) for x in q],
+        "config": {"workload": wl.name, "kind": wl.kind, "batch": wl.batch,
+                   "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+                   "head_dim_qk": wl.head_dim_qk, "head_dim_v": wl.head_dim_v,
+                   "block_size": wl.block_size, "num_shards": wl.num_shards,
+                   "tokens": bm["tokens"], "context_median": int(np.median(lens)),
+                   "kv_bytes": bm["kv"], "algorithmic_bytes_per_step": bm["step"],
+                   "parallelism": "all shards on one GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -32,7 +32,8 @@
  *    void*; NULL means the legacy default stream) and never synchronise.
  *  - All memory is owned by the caller. The library allocates no device
  *    memory and keeps no state beyond a per-device cache of launch
- *    parameters and the thread-local error string.
+ *    parameters, the thread-local error string and, between
+ *    dcp_kernel_timing_begin and _end, the calling thread's timing events.
  *  - Device pointers to Q, caches, partials, outputs and workspace must be
  *    16-byte aligned (the kernels use 128-bit loads and stores).
  *  - Values that only exist on the device (bounds, block-table entries) are
@@ -196,6 +197,18 @@ dcp_status dcp_debug_gather_shard(const dcp_attn_shape* shape, const void* cache
                                   const int32_t* block_table, const int32_t* bounds, int32_t b,
                                   int32_t s, int32_t kv_head, void* dst, int32_t max_rows,
                                   void* stream);
+
+/*
+ * Kernel timing for benchmarks (no effect on results). dcp_kernel_timing_begin(n) creates n
+ * pairs of HIP events; while timing is on for the calling thread, each of the next n
+ * dcp_decode_attn / dcp_decode_attn_partial calls records one pair around its
+ * partial-attention kernel, on the call's stream. dcp_kernel_timing_end() waits for the
+ * recorded events, returns how many launches were timed and their summed duration in
+ * milliseconds, and releases the events. Errors: DCP_ERR_SHAPE (n < 1), DCP_ERR_NULL,
+ * DCP_ERR_DEVICE.
+ */
+dcp_status dcp_kernel_timing_begin(int32_t max_launches);
+dcp_status dcp_kernel_timing_end(int32_t* launches, float* total_ms);
 
 #ifdef __cplusplus
 }

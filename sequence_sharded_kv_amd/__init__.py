@@ -26,6 +26,8 @@ from ._lib import (  # noqa: F401
     dcp_debug_gather_shard,
     dcp_decode_attn,
     dcp_decode_attn_partial,
+    dcp_kernel_timing_begin,
+    dcp_kernel_timing_end,
     dcp_last_error,
     dcp_merge_lse,
     dcp_plan_shards,

@@ -14,7 +14,14 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdcp.so")
 
-SOURCES = ["dcp_api.cpp", "k_util.hip", "k_gqa_valu.hip", "k_gqa_mfma.hip", "k_mla_mfma.hip"]
+# (source, object name, extra hipcc flags)
+SOURCES = [
+    ("dcp_api.cpp", "dcp_api", []),
+    ("k_util.hip", "k_util", []),
+    ("k_gqa_valu.hip", "k_gqa_valu", []),
+    ("k_gqa_mfma.hip", "k_gqa_mfma", []),
+    ("k_mla_mfma.hip", "k_mla_mfma", []),
+]
 
 # -packed-fp32-ops keeps hipcc from emitting packed fp32 VALU ops (v_pk_*_f32).
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
@@ -29,9 +36,10 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(spec, verbose: bool) -> str:
+    src, name, extra = spec
+    obj = os.path.join(BUILD, name + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, capture_output=True, text=True)

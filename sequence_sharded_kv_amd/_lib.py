@@ -34,6 +34,7 @@ EXPORTS = (
     "dcp_abi_version", "dcp_status_string", "dcp_last_error", "dcp_plan_shards",
     "dcp_plan_shards_device", "dcp_workspace_bytes", "dcp_decode_attn_partial", "dcp_merge_lse",
     "dcp_decode_attn", "dcp_read_device_flags", "dcp_debug_gather_shard",
+    "dcp_kernel_timing_begin", "dcp_kernel_timing_end",
 )
 
 
@@ -80,6 +81,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "dcp_decode_attn": (I32, [SH, P, P, P, P, P, P, SZ, P, P, P]),
         "dcp_read_device_flags": (I32, [P, ctypes.POINTER(I32), P]),
         "dcp_debug_gather_shard": (I32, [SH, P, P, P, I32, I32, I32, P, I32, P]),
+        "dcp_kernel_timing_begin": (I32, [I32]),
+        "dcp_kernel_timing_end": (I32, [ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_float)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -191,3 +194,15 @@ def dcp_debug_gather_shard(shape: dcp_attn_shape, cache, block_table, bounds, b:
     _check(load().dcp_debug_gather_shard(
         ctypes.byref(shape), _ptr(cache), _ptr(block_table), _ptr(bounds), b, s, kv_head,
         _ptr(dst), max_rows, _stream(cache)))
+
+
+def dcp_kernel_timing_begin(max_launches: int) -> None:
+    _check(load().dcp_kernel_timing_begin(max_launches))
+
+
+def dcp_kernel_timing_end():
+    """(launches timed, summed milliseconds) of the partial-attention kernel."""
+    n = ctypes.c_int32(0)
+    ms = ctypes.c_float(0.0)
+    _check(load().dcp_kernel_timing_end(ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)

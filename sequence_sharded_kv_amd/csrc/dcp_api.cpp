@@ -8,12 +8,30 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "dcp_internal.h"
 
 namespace {
 
 thread_local std::string g_last_error;
+
+// Benchmark timing: pre-created event pairs, filled one per timed launch.
+struct KernelTiming {
+  std::vector<hipEvent_t> start, stop;
+  size_t used = 0;
+  bool on = false;
+};
+thread_local KernelTiming g_timing;
+
+void destroy_timing_events() {
+  for (hipEvent_t e : g_timing.start) (void)hipEventDestroy(e);
+  for (hipEvent_t e : g_timing.stop) (void)hipEventDestroy(e);
+  g_timing.start.clear();
+  g_timing.stop.clear();
+  g_timing.used = 0;
+  g_timing.on = false;
+}
 
 dcp_status fail(dcp_status st, const char* fmt, ...) {
   char buf[512];
@@ -192,6 +210,11 @@ dcp_status run_partials(const dcp_attn_shape* sh, const void* q, const void* k, 
   e = dcp::launch_schedule(bounds, a.B, a.S, units_per_bs, a.bs, a.max_blocks,
                            const_cast<int32_t*>(a.ubounds), const_cast<int32_t*>(a.pre), a.flags, s);
   if (e != hipSuccess) return device_fail(e, "schedule launch");
+  const bool timed = g_timing.on && g_timing.used < g_timing.start.size();
+  if (timed) {
+    e = hipEventRecord(g_timing.start[g_timing.used], s);
+    if (e != hipSuccess) return device_fail(e, "timing event");
+  }
   switch (plan.kernel) {
     case dcp::Kernel::kGqaMfma: e = dcp::launch_gqa_mfma(a, s); break;
     case dcp::Kernel::kGqaValu: e = dcp::launch_gqa_valu(a, sh->dtype, s); break;
@@ -199,6 +222,10 @@ dcp_status run_partials(const dcp_attn_shape* sh, const void* q, const void* k, 
     default: break;
   }
   if (e != hipSuccess) return device_fail(e, "partial-attention launch");
+  if (timed) {
+    e = hipEventRecord(g_timing.stop[g_timing.used++], s);
+    if (e != hipSuccess) return device_fail(e, "timing event");
+  }
   e = dcp::launch_finish_units(a, plan.heads_per_unit, s);
   if (e != hipSuccess) return device_fail(e, "finish launch");
   *plan_out = plan;
@@ -338,6 +365,44 @@ dcp_status dcp_debug_gather_shard(const dcp_attn_shape* shape, const void* cache
   hipError_t e = dcp::launch_debug_gather(*shape, cache, block_table, bounds, b, s, kv_head, dst,
                                           max_rows, as_stream(stream));
   if (e != hipSuccess) return device_fail(e, "gather launch");
+  return ok();
+}
+
+dcp_status dcp_kernel_timing_begin(int32_t max_launches) {
+  if (max_launches < 1) return fail(DCP_ERR_SHAPE, "max_launches must be >= 1");
+  destroy_timing_events();
+  for (int32_t i = 0; i < max_launches; ++i) {
+    hipEvent_t a = nullptr, b = nullptr;
+    hipError_t e = hipEventCreate(&a);
+    if (e == hipSuccess) e = hipEventCreate(&b);
+    if (e != hipSuccess) {
+      if (a) (void)hipEventDestroy(a);
+      destroy_timing_events();
+      return device_fail(e, "hipEventCreate");
+    }
+    g_timing.start.push_back(a);
+    g_timing.stop.push_back(b);
+  }
+  g_timing.on = true;
+  return ok();
+}
+
+dcp_status dcp_kernel_timing_end(int32_t* launches, float* total_ms) {
+  if (!launches || !total_ms) return fail(DCP_ERR_NULL, "launches and total_ms must be non-NULL");
+  float sum = 0.f;
+  for (size_t i = 0; i < g_timing.used; ++i) {
+    hipError_t e = hipEventSynchronize(g_timing.stop[i]);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, g_timing.start[i], g_timing.stop[i]);
+    if (e != hipSuccess) {
+      destroy_timing_events();
+      return device_fail(e, "timing readback");
+    }
+    sum += ms;
+  }
+  *launches = (int32_t)g_timing.used;
+  *total_ms = sum;
+  destroy_timing_events();
   return ok();
 }
 

@@ -120,14 +120,17 @@ hipError_t launch_schedule(const int32_t* bounds, int32_t B, int32_t S, int32_t 
 // worker were written whole by the partial kernel. Units cut by worker boundaries have one
 // piece per covering worker; they are merged here by the LSE formula.
 constexpr int kFinishThreads = 256;
+constexpr int kFinishMaxPieces = 4096;  // >= the most workers any launch uses
 
 __global__ void __launch_bounds__(kFinishThreads)
 finish_units_kernel(AttnArgs a, int32_t Hu) {
+  __shared__ int32_t slots[kFinishMaxPieces];  // -1 for workers that own no pages
   const int32_t u = blockIdx.x;
   const int64_t T = a.pre[a.U];
   const int64_t p0 = a.pre[u], p1 = a.pre[u + 1];
-  const int32_t bsi = u / (a.U / (a.B * a.S));
-  const int32_t hsub = u % (a.U / (a.B * a.S));
+  const int32_t per_bs = a.U / (a.B * a.S);
+  const int32_t bsi = u / per_bs;
+  const int32_t hsub = u % per_bs;
   float* out_o = a.part_o + ((int64_t)bsi * a.Hq + (int64_t)hsub * Hu) * a.Dv;
   float* out_l = a.part_lse + (int64_t)bsi * a.Hq + (int64_t)hsub * Hu;
   const int32_t n = Hu * a.Dv;
@@ -138,24 +141,25 @@ finish_units_kernel(AttnArgs a, int32_t Hu) {
   }
   const int32_t w0 = worker_of(T, a.P, p0), w1 = worker_of(T, a.P, p1 - 1);
   if (w0 == w1) return;
-  // pieces: slot of worker w for this unit
+  // slot of each covering worker (empty workers wrote nothing)
+  const int32_t ns = w1 - w0 + 1;
+  for (int32_t k = threadIdx.x; k < ns; k += blockDim.x) {
+    const int32_t w = w0 + k;
+    const int64_t wb = worker_begin(T, a.P, w);
+    slots[k] = (worker_begin(T, a.P, w + 1) == wb) ? -1 : piece_slot(w, !(w == w0 && wb < p0));
+  }
+  __syncthreads();
   for (int32_t i = threadIdx.x; i < n; i += blockDim.x) {
     const int32_t h = i / a.Dv;
     float m = kNegInf;
-    for (int32_t w = w0; w <= w1; ++w) {
-      int64_t wb = worker_begin(T, a.P, w);
-      if (worker_begin(T, a.P, w + 1) == wb) continue;
-      int32_t slot = piece_slot(w, !(w == w0 && wb < p0));
-      m = fmaxf(m, a.piece_lse[(int64_t)slot * Hu + h]);
-    }
+    for (int32_t k = 0; k < ns; ++k)
+      if (slots[k] >= 0) m = fmaxf(m, a.piece_lse[(int64_t)slots[k] * Hu + h]);
     float den = 0.f, acc = 0.f;
-    for (int32_t w = w0; w <= w1; ++w) {
-      int64_t wb = worker_begin(T, a.P, w);
-      if (worker_begin(T, a.P, w + 1) == wb) continue;
-      int32_t slot = piece_slot(w, !(w == w0 && wb < p0));
-      float wt = safe_exp_diff(a.piece_lse[(int64_t)slot * Hu + h], m);
+    for (int32_t k = 0; k < ns; ++k) {
+      if (slots[k] < 0) continue;
+      const float wt = safe_exp_diff(a.piece_lse[(int64_t)slots[k] * Hu + h], m);
       den += wt;
-      acc += wt * a.piece_o[(int64_t)slot * n + i];
+      acc += wt * a.piece_o[(int64_t)slots[k] * n + i];
     }
     out_o[i] = den > 0.f ? acc / den : 0.f;
     if (i % a.Dv == 0) out_l[h] = den > 0.f ? m + logf(den) : kNegInf;
@@ -164,6 +168,7 @@ finish_units_kernel(AttnArgs a, int32_t Hu) {
 
 hipError_t launch_finish_units(const AttnArgs& a, int32_t Hu, hipStream_t stream) {
   if (a.U == 0) return hipSuccess;
+  if (a.P > kFinishMaxPieces) return hipErrorInvalidValue;
   hipLaunchKernelGGL(finish_units_kernel, dim3(a.U), dim3(kFinishThreads), 0, stream, a, Hu);
   return hipGetLastError();
 }

@@ -24,7 +24,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = dcp.load()
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(dcp.EXPORTS) == names
@@ -154,3 +154,5 @@ def test_merge_and_fused_error_paths():
     assert lib.dcp_debug_gather_shard(ctypes.byref(sh), 0x1000, 0x1000, 0x1000, 9, 0, 0, 0x1000, 4,
                                       None) == dcp.DCP_ERR_SHAPE
     assert lib.dcp_read_device_flags(None, None, None) == dcp.DCP_ERR_NULL
+    assert lib.dcp_kernel_timing_begin(0) == dcp.DCP_ERR_SHAPE
+    assert lib.dcp_kernel_timing_end(None, None) == dcp.DCP_ERR_NULL
