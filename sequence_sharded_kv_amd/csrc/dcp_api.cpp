@@ -134,6 +134,7 @@ dcp_status make_plan(const dcp_attn_shape* sh, dcp::Plan* plan) {
   size_t off = 0;
   w.flags = off;       off = align_up(off + dcp::kWsHeadBytes);
   w.pre = off;         off = align_up(off + sizeof(int32_t) * ((size_t)units + 1));
+  w.fin = off;         off = align_up(off + sizeof(int32_t) * 4 * (size_t)units);
   w.ubounds = off;     off = align_up(off + sizeof(int32_t) * B * S * 2);
   w.piece_o = off;     off = align_up(off + sizeof(float) * 2 * (size_t)pmax * hu * Dv);
   w.piece_lse = off;   off = align_up(off + sizeof(float) * 2 * (size_t)pmax * hu);
@@ -181,6 +182,7 @@ dcp_status run_partials(const dcp_attn_shape* sh, const void* q, const void* k, 
   a.block_table = block_table;
   a.ubounds = reinterpret_cast<int32_t*>(ws + plan.ws.ubounds);
   a.pre = reinterpret_cast<int32_t*>(ws + plan.ws.pre);
+  a.fin = reinterpret_cast<int32_t*>(ws + plan.ws.fin);
   a.part_o = fused ? reinterpret_cast<float*>(ws + plan.ws.part_o) : part_o;
   a.part_lse = fused ? reinterpret_cast<float*>(ws + plan.ws.part_lse) : part_lse;
   a.piece_o = reinterpret_cast<float*>(ws + plan.ws.piece_o);
@@ -207,7 +209,8 @@ dcp_status run_partials(const dcp_attn_shape* sh, const void* q, const void* k, 
   }
   hipStream_t s = as_stream(stream);
   const int32_t units_per_bs = plan.units / (sh->batch * sh->num_shards);
-  e = dcp::launch_schedule(bounds, a.B, a.S, units_per_bs, a.bs, a.max_blocks,
+  e = dcp::launch_schedule(bounds, a.B, a.S, units_per_bs, a.P,
+                           reinterpret_cast<int32_t*>(ws + plan.ws.fin), a.bs, a.max_blocks,
                            const_cast<int32_t*>(a.ubounds), const_cast<int32_t*>(a.pre), a.flags, s);
   if (e != hipSuccess) return device_fail(e, "schedule launch");
   const bool timed = g_timing.on && g_timing.used < g_timing.start.size();

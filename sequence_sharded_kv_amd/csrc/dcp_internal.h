@@ -25,16 +25,20 @@ constexpr int32_t kFlagBadBlock = 2;
 // finishing pass merges into the unit's partial.
 //
 // Workspace layout (offsets 256-byte aligned):
-//   flags      int32[64]  sticky device flag word at [0], then a 2 KB zero row at byte 256
-//                         (read in place of a page whose block id is invalid)
+//   flags      int32[64]  sticky device flag word at [0], the number of entries of `fin` at
+//                         [1], then a 2 KB zero row at byte 256 (read in place of a page
+//                         whose block id is invalid)
 //   pre        int32[U + 1]      exclusive prefix sum of unit page counts, pre[U] = T
+//   fin        int32[U][4]       units the finishing pass must write: (u, first worker, last
+//                                worker, 0) for units cut by worker boundaries, (u, -1, -1, 0)
+//                                for units with no pages; unordered
 //   ubounds    int32[B*S*2]      sanitised (start, end) per (request, shard)
 //   piece_o    float[2*Pmax][Hu][Dv]
 //   piece_lse  float[2*Pmax][Hu]
 //   part_o     float[B][S][Hq][Dv]   (fused path only)
 //   part_lse   float[B][S][Hq]
 struct WsLayout {
-  size_t flags, pre, ubounds, piece_o, piece_lse, part_o, part_lse, total;
+  size_t flags, pre, fin, ubounds, piece_o, piece_lse, part_o, part_lse, total;
 };
 
 enum class Kernel { kNone = 0, kGqaValu, kGqaMfma, kMlaMfma };
@@ -55,6 +59,7 @@ struct AttnArgs {
   const int32_t* block_table;
   const int32_t* ubounds;   // [B*S][2]
   const int32_t* pre;       // [U + 1]
+  const int32_t* fin;       // [U][4], count in flags[1]
   float* part_o;            // [B][S][Hq][Dv]
   float* part_lse;          // [B][S][Hq]
   float* piece_o;           // [2P][Hu][Dv]
@@ -69,6 +74,7 @@ struct AttnArgs {
 hipError_t launch_plan_device(const int32_t* seq_lens, int32_t B, int32_t S, int32_t bs,
                               int32_t* bounds, hipStream_t stream);
 hipError_t launch_schedule(const int32_t* bounds, int32_t B, int32_t S, int32_t units_per_bs,
+                           int32_t P, int32_t* fin,
                            int32_t bs, int32_t max_blocks, int32_t* ubounds, int32_t* pre,
                            int32_t* flags, hipStream_t stream);
 hipError_t launch_finish_units(const AttnArgs& a, int32_t Hu, hipStream_t stream);

@@ -36,18 +36,22 @@ hipError_t launch_plan_device(const int32_t* seq_lens, int32_t B, int32_t S, int
 
 // One workgroup: sanitise the bounds of every (request, shard), count each unit's pages and
 // write the exclusive prefix sum pre[0..U] (units ordered (b, s, h) with h < units_per_bs).
-// Also clears the flag word (the first call of a step owns it).
+// A second pass lists the units the finishing pass must write (cut by a worker boundary, or
+// without pages) in `fin`, with their count in flags[1]. Also clears the flag word (the
+// first call of a step owns it).
 constexpr int kSchedThreads = 1024;
 
 __global__ void __launch_bounds__(kSchedThreads)
 schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_t units_per_bs,
-                int32_t bs, int32_t max_blocks, int32_t* __restrict__ ubounds,
-                int32_t* __restrict__ pre, int32_t* __restrict__ flags) {
+                int32_t P, int32_t* __restrict__ fin, int32_t bs, int32_t max_blocks,
+                int32_t* __restrict__ ubounds, int32_t* __restrict__ pre,
+                int32_t* __restrict__ flags) {
   __shared__ int32_t warp_sums[kSchedThreads / 64];
   __shared__ int32_t carry;
   __shared__ int32_t flag_acc;
+  __shared__ int32_t fin_count;
   const int tid = threadIdx.x;
-  if (tid == 0) { carry = 0; flag_acc = 0; }
+  if (tid == 0) { carry = 0; flag_acc = 0; fin_count = 0; }
   for (int i = tid; i < kWsZeroWords; i += kSchedThreads) flags[kWsZeroOffset / 4 + i] = 0;
   __syncthreads();
   const int64_t cap = (int64_t)max_blocks * bs;
@@ -99,77 +103,106 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
     __syncthreads();
   }
   if (my_flag) atomicOr(&flag_acc, my_flag);
+  if (tid == 0) pre[U] = carry;
+  __syncthreads();  // pre[] is complete and visible to the workgroup
+  const int64_t T = carry;
+  for (int64_t u = tid; u < U; u += kSchedThreads) {
+    const int64_t p0 = pre[u], p1 = pre[u + 1];
+    int32_t w0 = -1, w1 = -1;
+    if (p1 > p0) {
+      w0 = worker_of(T, P, p0);
+      w1 = worker_of(T, P, p1 - 1);
+      if (w0 == w1) continue;  // written whole by its worker
+    }
+    const int32_t k = atomicAdd(&fin_count, 1);
+    *(i32x4*)(fin + 4 * (int64_t)k) = i32x4{(int32_t)u, w0, w1, 0};
+  }
   __syncthreads();
   if (tid == 0) {
-    pre[U] = carry;
     flags[0] = flag_acc;
+    flags[1] = fin_count;
   }
 }
 
 hipError_t launch_schedule(const int32_t* bounds, int32_t B, int32_t S, int32_t units_per_bs,
-                           int32_t bs, int32_t max_blocks, int32_t* ubounds, int32_t* pre,
-                           int32_t* flags, hipStream_t stream) {
+                           int32_t P, int32_t* fin, int32_t bs, int32_t max_blocks,
+                           int32_t* ubounds, int32_t* pre, int32_t* flags, hipStream_t stream) {
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, bounds, B, S,
-                     units_per_bs, bs, max_blocks, ubounds, pre, flags);
+                     units_per_bs, P, fin, bs, max_blocks, ubounds, pre, flags);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- finish units
 
-// One workgroup per unit. Units with no pages get O = 0, LSE = -inf. Units covered by one
-// worker were written whole by the partial kernel. Units cut by worker boundaries have one
-// piece per covering worker; they are merged here by the LSE formula.
+// Writes the partial of every unit in the schedule's `fin` list. A unit with no pages gets
+// O = 0, LSE = -inf. A unit cut by worker boundaries left one piece per covering worker
+// (none from a worker whose range is empty); the pieces are merged by the LSE formula.
+// Grid (x, c): workgroup x takes list entries x, x + gridDim.x, ...; chunk c is 1024
+// consecutive output floats of the unit (one float4 per thread).
 constexpr int kFinishThreads = 256;
 constexpr int kFinishMaxPieces = 4096;  // >= the most workers any launch uses
 
 __global__ void __launch_bounds__(kFinishThreads)
 finish_units_kernel(AttnArgs a, int32_t Hu) {
   __shared__ int32_t slots[kFinishMaxPieces];  // -1 for workers that own no pages
-  const int32_t u = blockIdx.x;
+  const int32_t count = a.flags[1];
   const int64_t T = a.pre[a.U];
-  const int64_t p0 = a.pre[u], p1 = a.pre[u + 1];
   const int32_t per_bs = a.U / (a.B * a.S);
-  const int32_t bsi = u / per_bs;
-  const int32_t hsub = u % per_bs;
-  float* out_o = a.part_o + ((int64_t)bsi * a.Hq + (int64_t)hsub * Hu) * a.Dv;
-  float* out_l = a.part_lse + (int64_t)bsi * a.Hq + (int64_t)hsub * Hu;
-  const int32_t n = Hu * a.Dv;
-  if (p1 == p0) {
-    for (int32_t i = threadIdx.x; i < n; i += blockDim.x) out_o[i] = 0.f;
-    for (int32_t i = threadIdx.x; i < Hu; i += blockDim.x) out_l[i] = kNegInf;
-    return;
-  }
-  const int32_t w0 = worker_of(T, a.P, p0), w1 = worker_of(T, a.P, p1 - 1);
-  if (w0 == w1) return;
-  // slot of each covering worker (empty workers wrote nothing)
-  const int32_t ns = w1 - w0 + 1;
-  for (int32_t k = threadIdx.x; k < ns; k += blockDim.x) {
-    const int32_t w = w0 + k;
-    const int64_t wb = worker_begin(T, a.P, w);
-    slots[k] = (worker_begin(T, a.P, w + 1) == wb) ? -1 : piece_slot(w, !(w == w0 && wb < p0));
-  }
-  __syncthreads();
-  for (int32_t i = threadIdx.x; i < n; i += blockDim.x) {
-    const int32_t h = i / a.Dv;
+  const int32_t n4 = Hu * a.Dv / 4;
+  const int32_t i4 = blockIdx.y * kFinishThreads + threadIdx.x;
+  const int32_t h = 4 * i4 / a.Dv;
+  const bool head_start = (4 * i4) % a.Dv == 0;
+  for (int32_t e = blockIdx.x; e < count; e += gridDim.x) {
+    const i32x4 ent = *(const i32x4*)(a.fin + 4 * (int64_t)e);
+    const int32_t u = ent[0], w0 = ent[1], w1 = ent[2];
+    const int32_t bsi = u / per_bs, hsub = u % per_bs;
+    float* out_o = a.part_o + ((int64_t)bsi * a.Hq + (int64_t)hsub * Hu) * a.Dv;
+    float* out_l = a.part_lse + (int64_t)bsi * a.Hq + (int64_t)hsub * Hu;
+    if (w0 < 0) {
+      if (i4 < n4) {
+        ((f32x4*)out_o)[i4] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (head_start) out_l[h] = kNegInf;
+      }
+      continue;
+    }
+    const int64_t p0 = a.pre[u];
+    const int32_t ns = w1 - w0 + 1;
+    __syncthreads();  // slots of the previous entry are no longer read
+    for (int32_t k = threadIdx.x; k < ns; k += kFinishThreads) {
+      const int32_t w = w0 + k;
+      const int64_t wb = worker_begin(T, a.P, w);
+      slots[k] = (worker_begin(T, a.P, w + 1) == wb) ? -1 : piece_slot(w, !(w == w0 && wb < p0));
+    }
+    __syncthreads();
+    if (i4 >= n4) continue;
     float m = kNegInf;
     for (int32_t k = 0; k < ns; ++k)
       if (slots[k] >= 0) m = fmaxf(m, a.piece_lse[(int64_t)slots[k] * Hu + h]);
-    float den = 0.f, acc = 0.f;
+    float den = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int32_t k = 0; k < ns; ++k) {
-      if (slots[k] < 0) continue;
-      const float wt = safe_exp_diff(a.piece_lse[(int64_t)slots[k] * Hu + h], m);
+      const int32_t sl = slots[k];
+      if (sl < 0) continue;
+      const float wt = safe_exp_diff(a.piece_lse[(int64_t)sl * Hu + h], m);
+      const f32x4 o = ((const f32x4*)(a.piece_o + (int64_t)sl * Hu * a.Dv))[i4];
       den += wt;
-      acc += wt * a.piece_o[(int64_t)slots[k] * n + i];
+      acc += wt * o;
     }
-    out_o[i] = den > 0.f ? acc / den : 0.f;
-    if (i % a.Dv == 0) out_l[h] = den > 0.f ? m + logf(den) : kNegInf;
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    ((f32x4*)out_o)[i4] = acc * inv;
+    if (head_start) out_l[h] = den > 0.f ? m + logf(den) : kNegInf;
   }
 }
 
 hipError_t launch_finish_units(const AttnArgs& a, int32_t Hu, hipStream_t stream) {
   if (a.U == 0) return hipSuccess;
   if (a.P > kFinishMaxPieces) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(finish_units_kernel, dim3(a.U), dim3(kFinishThreads), 0, stream, a, Hu);
+  const int32_t n4 = Hu * a.Dv / 4;
+  const int32_t chunks = (n4 + kFinishThreads - 1) / kFinishThreads;
+  int32_t x = (4096 + chunks - 1) / chunks;
+  if (x > a.U) x = a.U;
+  hipLaunchKernelGGL(finish_units_kernel, dim3(x, chunks), dim3(kFinishThreads), 0, stream, a,
+                     Hu);
   return hipGetLastError();
 }
 
@@ -193,12 +226,12 @@ merge_kernel(int32_t B, int32_t S, int32_t H, int32_t Dv, const float* __restric
   float den = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int32_t s = 0; s < S; ++s) {
-    float w = safe_exp_diff(lse[(int64_t)s * H], m);
+    // Loads are unconditional so that all S of them are in flight together; a shard with
+    // zero weight (LSE = -inf) contributes nothing whatever its O holds.
+    const float w = safe_exp_diff(lse[(int64_t)s * H], m);
+    const f32x4 o = *(const f32x4*)(part_o + ((b * S + s) * H + h) * Dv + 4 * c);
     den += w;
-    if (w != 0.f) {
-      const f32x4 o = *(const f32x4*)(part_o + ((b * S + s) * H + h) * Dv + 4 * c);
-      acc += w * o;
-    }
+    if (w != 0.f) acc += w * o;
   }
   float inv = den > 0.f ? 1.f / den : 0.f;
   *(f32x4*)(out + bh * Dv + 4 * c) = acc * inv;
