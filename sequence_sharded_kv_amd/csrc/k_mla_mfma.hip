@@ -15,7 +15,7 @@
 //     into a bf16 high part and a bf16 remainder, two MFMAs).
 //
 // LDS tile layout (36.5 KB): region A = dims 0..511 of the 32 rows, one 1 KB row per DMA
-// instruction, rows padded to 1040 B; region B = dims 512..575, 128 B per row with the 16-byte
+// instruction, rows padded to 1056 B; region B = dims 512..575, 128 B per row with the 16-byte
 // chunks XOR-swizzled by row. MFMA row m of a 16-row subtile is token pi(m), where
 // pi(8c + 4h + e) = 8c + h + 2e: the K reads of 8 consecutive MFMA rows then touch 8
 // different 16-byte bank groups, and each transposed V read (4 MFMA rows e = 0..3) reads
@@ -27,7 +27,7 @@ namespace dcp {
 constexpr int kMlaDqk = 576;
 constexpr int kMlaDv = 512;
 constexpr int kMlaTile = 32;
-constexpr int kMlaRowA = 1040;                    // LDS bytes per row, region A (dims 0..511)
+constexpr int kMlaRowA = 1056;                    // LDS bytes per row, region A (dims 0..511)
 constexpr int kMlaRowB = 128;                     // LDS bytes per row, region B (dims 512..575)
 constexpr int kMlaRegionB = kMlaTile * kMlaRowA;  // offset of region B
 constexpr int kMlaTileBytes = kMlaRegionB + kMlaTile * kMlaRowB;
@@ -49,10 +49,19 @@ __device__ __forceinline__ bf16x8 mla_tr_pair(const char* lo, const char* hi) {
   return __builtin_bit_cast(bf16x8, z);
 }
 
-__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
-  uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src, 64);
-  uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src, 64);
-  return ((uint64_t)hi << 32) | lo;
+// max / sum over the four lanes n, n+16, n+32, n+48 that hold one head, with the VALU lane
+// swaps of gfx950 (cross-lane LDS operations would queue behind the tile reads)
+__device__ __forceinline__ float quad_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
@@ -61,12 +70,36 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Queue one 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane i's 16 bytes
+// land at LDS byte address lds_addr + 16 i. Written as inline asm so that the compiler does
+// not treat every later LDS read as possibly overwritten by it (it would otherwise wait for
+// the next tile's copies before the first transposed read of the current tile); completion
+// is awaited explicitly with vmcnt(0) before the barrier that publishes a tile. M0 is saved
+// and restored.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);  // wave-uniform by contract
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(m0v)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
 template <int NW>  // waves per workgroup; 16 heads per wave, Hq = 16 * NW
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
   __shared__ __attribute__((aligned(1024))) char lds[2][kMlaTileBytes];
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
   const int n = lane & 15;        // head within the wave; also the MFMA row this lane loads
   const int gq = lane >> 4;       // lane quarter (k-slice of the operand layouts)
   const int32_t w = blockIdx.x;
@@ -101,34 +134,51 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
     const bool first = (g == g0);
     const int32_t* brow = a.block_table + (int64_t)b * a.max_blocks;
 
+    // Block id of the page holding token tile + (lane & 31), read one tile ahead of its use:
+    // the load's wait then falls after the previous tile's barrier, when nothing else is in
+    // flight.
+    // Token positions fit in 32 bits (max_blocks_per_seq * block_size <= INT32_MAX).
+    const int32_t t0i = (int32_t)t0, t1i = (int32_t)t1;
+    auto page_of = [&](int32_t tile) -> int32_t {
+      const int32_t t = tile + (lane & 31);
+      return brow[(t < t1i ? t : t1i - 1) / a.bs];
+    };
+    int32_t blk_next = page_of(t0i);
+
     // Queue the copy of tile [tile, tile + 32) into buffer `buf`; returns the valid-token mask.
-    auto issue_tile = [&](int64_t tile, int buf) -> uint32_t {
+    auto issue_tile = [&](int32_t tile, int buf) -> uint32_t {
+      const int32_t blk = blk_next;
+      if (tile + kMlaTile < t1i) blk_next = page_of(tile + kMlaTile);
       uint64_t rowaddr = (uint64_t)zero_row;
       bool valid = false;
       if (lane < kMlaTile) {
-        int64_t t = tile + lane;
-        int64_t tc = t < t1 ? t : t1 - 1;
-        int32_t blk = brow[tc / a.bs];
-        bool page_ok = blk >= 0 && blk < a.num_blocks;
+        const int32_t t = tile + lane;
+        const int32_t tc = t < t1i ? t : t1i - 1;
+        const bool page_ok = blk >= 0 && blk < a.num_blocks;
+        // row index < num_blocks * block_size rows of 1152 B: below 2^31 for any pool that
+        // fits in device memory
+        const uint32_t row = (uint32_t)blk * (uint32_t)a.bs + (uint32_t)(tc % a.bs);
         if (page_ok)
-          rowaddr = (uint64_t)(Kc + ((int64_t)blk * a.bs + tc % a.bs) * (kMlaDqk * 2));
+          rowaddr = (uint64_t)Kc + (uint64_t)row * (kMlaDqk * 2);
         else
           bad = 1;
-        valid = page_ok && t < t1;
+        valid = page_ok && t < t1i;
       }
       const uint32_t mask = (uint32_t)__ballot(valid);
-      char* base = &lds[buf][0];
-      for (int r = wv; r < kMlaTile; r += NW) {
-        const char* src = (const char*)readlane_u64(rowaddr, r) + 16 * lane;
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(base + r * kMlaRowA), 16,
-                                         0, 0);
-      }
+      const uint32_t base = lds_u32(&lds[buf][0]);
+      for (int r = wv; r < kMlaTile; r += NW)
+        dma16((const char*)readlane_u64(rowaddr, r) + 16 * lane, base + r * kMlaRowA);
       for (int kk = wv; kk < 4; kk += NW) {
+        // lane covers row 8 kk + lane / 8: pick its address among the eight rows' addresses
+        uint64_t ra = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint64_t aj = readlane_u64(rowaddr, 8 * kk + j);
+          ra = ((lane >> 3) == j) ? aj : ra;
+        }
         const int r = 8 * kk + (lane >> 3);
-        const uint64_t ra = shfl_u64(rowaddr, r);
-        const char* src = (const char*)ra + 1024 + 16 * ((lane & 7) ^ swz_b(r));
-        __builtin_amdgcn_global_load_lds((const void*)src,
-                                         (lds_void_t*)(base + kMlaRegionB + kk * 1024), 16, 0, 0);
+        dma16((const char*)ra + 1024 + 16 * ((lane & 7) ^ swz_b(r)),
+              base + kMlaRegionB + kk * 1024);
       }
       return mask;
     };
@@ -147,12 +197,13 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
     for (int i = 0; i < kMlaDv / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = kNegInf, l_run = 0.f;
 
-    uint32_t mask_next = issue_tile(t0, 0);
+    uint32_t mask_next = issue_tile(t0i, 0);
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) lgkmcnt(0): the copies of the first tile
     __syncthreads();
     int cur = 0;
-    for (int64_t tile = t0; tile < t1; tile += kMlaTile) {
+    for (int32_t tile = t0i; tile < t1i; tile += kMlaTile) {
       const uint32_t mask = mask_next;
-      if (tile + kMlaTile < t1) mask_next = issue_tile(tile + kMlaTile, cur ^ 1);
+      if (tile + kMlaTile < t1i) mask_next = issue_tile(tile + kMlaTile, cur ^ 1);
       const char* tb = &lds[cur][0];
 
       // S^T = K . Q^T for the two 16-row subtiles
@@ -184,8 +235,7 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
           x[4 * at + i] = v;
           tmax = fmaxf(tmax, v);
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = quad_max(tmax);
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
       float psum = 0.f;
@@ -215,14 +265,13 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo, acc[mt], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) lgkmcnt(0): the next tile's copies landed
       __syncthreads();
       cur ^= 1;
     }
 
     // finalise this segment: l over the four lanes of head n
-    float l = l_run;
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = quad_sum(l_run);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int head = 16 * wv + n;
     float* dst_o;
