@@ -6,13 +6,15 @@
 //                                                     straight from HBM as the A operand,
 //                                                     Q of the group held as the B operand;
 //   online softmax per head (column of S^T): each lane holds 8 scores of one head, the max
-//   and the sums need two cross-lane shuffles;
+//   and the sums are reduced over the head's four lanes with lane swaps;
 //   O^T[D x 16] += V^T[D x 32] . P^T[32 x 16]          V staged row-major in the wave's own
 //                                                     LDS tile and read back transposed with
 //                                                     ds_read_b64_tr_b16; P from registers.
 // P is split into a bf16 high part and a bf16 remainder (two MFMAs) so that the weights
 // carry about 16 mantissa bits; rounding P to one bf16 alone would cost ~1e-3 relative error.
-// The next tile's K and V loads are issued before the current tile is computed.
+// K and V of the next tile sit in a second register set whose loads are queued before the
+// current tile is computed (their block ids were read one tile earlier still), so every wave
+// keeps a whole tile in flight; at 244 registers two waves share each SIMD.
 #include "device_common.h"
 
 namespace dcp {
@@ -25,7 +27,6 @@ struct GqaCfg {
   static constexpr int kSteps = D / 32;          // MFMA k-steps for Q.K
   static constexpr int kMt = D / 16;             // M tiles of O^T
   static constexpr int kRowBytes = D * 2 + 32;   // padded LDS row of the V tile
-  static constexpr int kVChunks = kGqaTile * D * 2 / 16 / 64;  // 16-byte V chunks per lane
   static constexpr int kLdsPerWave = kGqaTile * kRowBytes;
 };
 
@@ -39,14 +40,38 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* lo, const char* hi) {
   return __builtin_bit_cast(bf16x8, z);
 }
 
+// max / sum over the four lanes n, n+16, n+32, n+48 that hold one head, with the VALU lane
+// swaps of gfx950 (no LDS round trip)
+__device__ __forceinline__ float gqa_quad_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float gqa_quad_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// The K and V registers of one tile: lane (n, gq) holds, for its tokens tile + n and
+// tile + 16 + n, K dims 32 j + 8 gq .. +8 (the MFMA A operand) and V chunks gq, gq + 4, ...
 template <int D>
-__global__ void __launch_bounds__(64 * kGqaWaves)
+struct GqaTileRegs {
+  u32x4 k[2][GqaCfg<D>::kSteps];
+  u32x4 v[2][D / 32];
+  uint32_t mask;  // bit r: token tile + r is valid
+};
+
+template <int D>
+__global__ void __launch_bounds__(64 * kGqaWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gqa_mfma_kernel(AttnArgs a) {
   using C = GqaCfg<D>;
   extern __shared__ char gqa_lds[];
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int n = lane & 15;       // head within the group / token row within an M tile
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;       // head within the group / token row within a subtile
   const int gq = lane >> 4;      // lane quarter
   char* vt = gqa_lds + wv * C::kLdsPerWave;
   const int32_t w = blockIdx.x * kGqaWaves + wv;
@@ -58,6 +83,9 @@ gqa_mfma_kernel(AttnArgs a) {
   const int64_t g0 = worker_begin(T_pages, a.P, w), g1 = worker_begin(T_pages, a.P, w + 1);
   if (g0 >= g1) return;
   const int G = a.G;
+  const int32_t bs = a.bs;
+  const bool bs_pow2 = (bs & (bs - 1)) == 0;
+  const int bs_shift = __builtin_ctz((unsigned)bs);
   int32_t u = find_unit(a.pre, a.U, g0);
   int64_t g = g0;
   int32_t bad = 0;
@@ -69,13 +97,15 @@ gqa_mfma_kernel(AttnArgs a) {
     const int32_t bsi = u / a.Hkv, kvh = u % a.Hkv;
     const int32_t b = bsi / a.S;
     const int64_t ta = a.ubounds[2 * bsi], te = a.ubounds[2 * bsi + 1];
-    const int64_t pa = ta / a.bs;
-    int64_t t0 = (pa + (g - up0)) * a.bs, t1 = (pa + (sg1 - up0)) * a.bs;
+    const int64_t pa = ta / bs;
+    int64_t t0 = (pa + (g - up0)) * bs, t1 = (pa + (sg1 - up0)) * bs;
     if (t0 < ta) t0 = ta;
     if (t1 > te) t1 = te;
     const bool whole = (g == up0) && (sg1 == up1);
     const bool first = (g == g0);
     const int32_t* brow = a.block_table + (int64_t)b * a.max_blocks;
+    // Token positions fit in 32 bits (max_blocks_per_seq * block_size <= INT32_MAX).
+    const int32_t t0i = (int32_t)t0, t1i = (int32_t)t1;
 
     // Q^T as the B operand: lane (n, gq) holds q[n][32j + 8gq .. +8]
     bf16x8 qop[C::kSteps];
@@ -90,41 +120,42 @@ gqa_mfma_kernel(AttnArgs a) {
       }
     }
 
-    // row address of token t of this unit (clamped into the segment; invalid pages -> -1)
-    auto row_of = [&](int64_t t) -> int64_t {
-      if (t >= t1) t = t1 - 1;
-      int32_t blk = brow[t / a.bs];
-      if (blk < 0 || blk >= a.num_blocks) return -1;
-      return (((int64_t)blk * a.Hkv + kvh) * a.bs + t % a.bs) * D;
-    };
-
-    u32x4 kreg[2][C::kSteps];
-    u32x4 vreg[C::kVChunks];
-    uint32_t vmask = 0;  // bit r: token tile+r is valid
-    auto load_tile = [&](int64_t tile) {
-      // K: lane loads token tile + 16a + n, dims 32j + 8gq
+    auto page_idx = [&](int32_t t) -> int32_t { return bs_pow2 ? (t >> bs_shift) : t / bs; };
+    auto slot_of = [&](int32_t t) -> int32_t { return bs_pow2 ? (t & (bs - 1)) : t % bs; };
+    // block ids of this lane's two tokens of a tile (clamped into the segment)
+    auto pages_of = [&](int32_t tile, int32_t* pg) {
 #pragma unroll
       for (int at = 0; at < 2; ++at) {
-        int64_t t = tile + 16 * at + n;
-        int64_t r = row_of(t);
-        bool ok = (t < t1) && (r >= 0);
-        uint64_t bal = __ballot(ok);
-        if (at == 0) vmask = (uint32_t)(bal & 0xFFFF); else vmask |= (uint32_t)(bal & 0xFFFF) << 16;
-        if (r < 0) { bad |= (t < t1); r = 0; }
-        const uint16_t* kp = K + r;
-#pragma unroll
-        for (int j = 0; j < C::kSteps; ++j) kreg[at][j] = *(const u32x4*)(kp + 32 * j + 8 * gq);
+        int32_t t = tile + 16 * at + n;
+        if (t >= t1i) t = t1i - 1;
+        pg[at] = brow[page_idx(t)];
       }
-      // V: chunk c = lane + 64i covers token c / (D/8), dims 8 (c % (D/8))
+    };
+    // queue the loads of tile `tile` whose tokens' block ids are pg
+    auto load_tile = [&](int32_t tile, const int32_t* pg, GqaTileRegs<D>& r) {
+      uint32_t m = 0;
 #pragma unroll
-      for (int i = 0; i < C::kVChunks; ++i) {
-        int c = lane + 64 * i;
-        int tr = c / (D / 8), col = c % (D / 8);
-        int64_t r = row_of(tile + tr);
-        u32x4 x = {0, 0, 0, 0};
-        if (r >= 0) x = *(const u32x4*)(V + r + 8 * col);
-        vreg[i] = x;
+      for (int at = 0; at < 2; ++at) {
+        int32_t t = tile + 16 * at + n;
+        const bool in = t < t1i;
+        if (!in) t = t1i - 1;
+        const int32_t blk = pg[at];
+        const bool page_ok = blk >= 0 && blk < a.num_blocks;
+        bad |= (in && !page_ok) ? 1 : 0;
+        const uint64_t bal = __ballot(in && page_ok);
+        m |= (uint32_t)(bal & 0xFFFF) << (16 * at);
+        // row index (block, kv head, slot) of the token; a token of an invalid page reads the
+        // workspace's zero row and is masked out
+        const uint32_t row = ((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)kvh) * (uint32_t)bs +
+                             (uint32_t)slot_of(t);
+        const uint16_t* kp = page_ok ? K + (uint64_t)row * D : (const uint16_t*)a.zero_row;
+        const uint16_t* vp = page_ok ? V + (uint64_t)row * D : (const uint16_t*)a.zero_row;
+#pragma unroll
+        for (int j = 0; j < C::kSteps; ++j) r.k[at][j] = *(const u32x4*)(kp + 32 * j + 8 * gq);
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) r.v[at][i] = *(const u32x4*)(vp + 8 * (4 * i + gq));
       }
+      r.mask = m;
     };
 
     f32x4 acc[C::kMt];
@@ -132,23 +163,24 @@ gqa_mfma_kernel(AttnArgs a) {
     for (int i = 0; i < C::kMt; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = kNegInf, l_run = 0.f;
 
-    load_tile(t0);
-    for (int64_t tile = t0; tile < t1; tile += kGqaTile) {
-      u32x4 kcur[2][C::kSteps];
+    // One tile: stage V of `cur` in LDS, queue the loads of the next tile into `nxt` (its
+    // block ids were read one tile earlier), read the block ids of the tile after it, then
+    // scores, softmax and P.V of `cur`.
+    int32_t pg_next[2], pg_after[2];
+    auto step = [&](int32_t tile, GqaTileRegs<D>& cur, GqaTileRegs<D>& nxt) {
 #pragma unroll
       for (int at = 0; at < 2; ++at)
 #pragma unroll
-        for (int j = 0; j < C::kSteps; ++j) kcur[at][j] = kreg[at][j];
-      const uint32_t mask = vmask;
-      // stage V of this tile into the wave's LDS tile
-#pragma unroll
-      for (int i = 0; i < C::kVChunks; ++i) {
-        int c = lane + 64 * i;
-        int tr = c / (D / 8), col = c % (D / 8);
-        *(u32x4*)(vt + tr * C::kRowBytes + col * 16) = vreg[i];
+        for (int i = 0; i < D / 32; ++i)
+          *(u32x4*)(vt + (16 * at + n) * C::kRowBytes + (4 * i + gq) * 16) = cur.v[at][i];
+      if (tile + kGqaTile < t1i) {
+        load_tile(tile + kGqaTile, pg_next, nxt);
+        if (tile + 2 * kGqaTile < t1i) {
+          pages_of(tile + 2 * kGqaTile, pg_after);
+          pg_next[0] = pg_after[0];
+          pg_next[1] = pg_after[1];
+        }
       }
-      if (tile + kGqaTile < t1) load_tile(tile + kGqaTile);
-
       // S^T = K . Q^T
       f32x4 s[2];
 #pragma unroll
@@ -156,32 +188,32 @@ gqa_mfma_kernel(AttnArgs a) {
         s[at] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < C::kSteps; ++j)
-          s[at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kcur[at][j]),
+          s[at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[at][j]),
                                                           qop[j], s[at], 0, 0, 0);
       }
       // online softmax: lane holds tokens 16at + 4gq + i of head n
+      const uint32_t mask = cur.mask;
       float x[8];
       float tmax = kNegInf;
 #pragma unroll
       for (int at = 0; at < 2; ++at)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          int tok = 16 * at + 4 * gq + i;
-          float v = ((mask >> tok) & 1u) ? s[at][i] * a.scale_log2 : kNegInf;
+          const int tok = 16 * at + 4 * gq + i;
+          const float v = ((mask >> tok) & 1u) ? s[at][i] * a.scale_log2 : kNegInf;
           x[4 * at + i] = v;
           tmax = fmaxf(tmax, v);
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = gqa_quad_max(tmax);
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
       float psum = 0.f;
       bf16x8 phi, plo;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        float p = (x[k] == kNegInf) ? 0.f : fast_exp2(x[k] - m_new);
+        const float p = (x[k] == kNegInf) ? 0.f : fast_exp2(x[k] - m_new);
         psum += p;
-        __bf16 h = (__bf16)p;
+        const __bf16 h = (__bf16)p;
         phi[k] = h;
         plo[k] = (__bf16)(p - (float)h);
       }
@@ -192,21 +224,30 @@ gqa_mfma_kernel(AttnArgs a) {
         for (int i = 0; i < C::kMt; ++i) acc[i] *= alpha;
       }
       // O^T += V^T . P^T ; A operand rows: tokens 4gq + e (slots 0..3), 16 + 4gq + e (4..7)
-      const int qi = lane & 15;
-      const char* rlo = vt + (4 * gq + (qi >> 2)) * C::kRowBytes + (qi & 3) * 8;
+      const char* rlo = vt + (4 * gq + (n >> 2)) * C::kRowBytes + (n & 3) * 8;
       const char* rhi = rlo + 16 * C::kRowBytes;
 #pragma unroll
       for (int mt = 0; mt < C::kMt; ++mt) {
-        bf16x8 vop = tr_pair(rlo + mt * 32, rhi + mt * 32);
+        const bf16x8 vop = tr_pair(rlo + mt * 32, rhi + mt * 32);
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi, acc[mt], 0, 0, 0);
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo, acc[mt], 0, 0, 0);
       }
+    };
+
+    GqaTileRegs<D> ra, rb;
+    {
+      int32_t pg0[2];
+      pages_of(t0i, pg0);
+      load_tile(t0i, pg0, ra);
+      if (t0i + kGqaTile < t1i) pages_of(t0i + kGqaTile, pg_next);
+    }
+    for (int32_t tile = t0i; tile < t1i; tile += 2 * kGqaTile) {
+      step(tile, ra, rb);
+      if (tile + kGqaTile < t1i) step(tile + kGqaTile, rb, ra);
     }
 
     // finalise: l over the four lanes of head n
-    float l = l_run;
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = gqa_quad_sum(l_run);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     float* dst_o;
     float* dst_l;
