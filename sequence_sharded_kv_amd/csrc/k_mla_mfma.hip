@@ -145,8 +145,21 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
     };
     int32_t blk_next = page_of(t0i);
 
-    // Queue the copy of tile [tile, tile + 32) into buffer `buf`; returns the valid-token mask.
-    auto issue_tile = [&](int32_t tile, int buf) -> uint32_t {
+    // A wave copies region-A rows wv + k NW (k < kRows) of each tile. Inside the tile loop it
+    // queues half of them before the scores and the other half after: a wave that queues a
+    // whole tile at once stalls on the memory pipeline's back-pressure instead of computing.
+    // The rows' source addresses are wave-uniform and held in scalar registers in between.
+    constexpr int kRows = kMlaTile / NW;
+    uint64_t row_src[kRows];
+    uint32_t base_pend = 0;
+    auto issue_rows = [&](int k0, int k1) {
+#pragma unroll
+      for (int k = k0; k < k1; ++k)
+        dma16((const char*)row_src[k] + 16 * lane, base_pend + (wv + k * NW) * kMlaRowA);
+    };
+    // Queue the copy of tile [tile, tile + 32) into buffer `buf` (all region-A rows, or the
+    // first half of them with the rest left to issue_rows); returns the valid-token mask.
+    auto issue_tile = [&](int32_t tile, int buf, bool all) -> uint32_t {
       const int32_t blk = blk_next;
       if (tile + kMlaTile < t1i) blk_next = page_of(tile + kMlaTile);
       uint64_t rowaddr = (uint64_t)zero_row;
@@ -166,8 +179,10 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
       }
       const uint32_t mask = (uint32_t)__ballot(valid);
       const uint32_t base = lds_u32(&lds[buf][0]);
-      for (int r = wv; r < kMlaTile; r += NW)
-        dma16((const char*)readlane_u64(rowaddr, r) + 16 * lane, base + r * kMlaRowA);
+#pragma unroll
+      for (int k = 0; k < kRows; ++k) row_src[k] = readlane_u64(rowaddr, wv + k * NW);
+      base_pend = base;
+      issue_rows(0, all ? kRows : kRows / 2);
       for (int kk = wv; kk < 4; kk += NW) {
         // lane covers row 8 kk + lane / 8: pick its address among the eight rows' addresses
         uint64_t ra = 0;
@@ -197,13 +212,15 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
     for (int i = 0; i < kMlaDv / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = kNegInf, l_run = 0.f;
 
-    uint32_t mask_next = issue_tile(t0i, 0);
+    uint32_t mask_next = issue_tile(t0i, 0, true);
     __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) lgkmcnt(0): the copies of the first tile
     __syncthreads();
     int cur = 0;
     for (int32_t tile = t0i; tile < t1i; tile += kMlaTile) {
       const uint32_t mask = mask_next;
-      if (tile + kMlaTile < t1i) mask_next = issue_tile(tile + kMlaTile, cur ^ 1);
+      constexpr int kQ = kRows / 2;  // rows queued before the scores
+      const bool more = tile + kMlaTile < t1i;
+      if (more) mask_next = issue_tile(tile + kMlaTile, cur ^ 1, false);
       const char* tb = &lds[cur][0];
 
       // S^T = K . Q^T for the two 16-row subtiles
@@ -223,6 +240,7 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
         }
       }
 
+      if (more) issue_rows(kQ, kRows);
       // online softmax; s[at][i] is MFMA row 4gq + i of subtile at (token 16at + pi(4gq + i))
       float x[8];
       float tmax = kNegInf;
