@@ -112,6 +112,8 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
   int32_t u = find_unit(a.pre, a.U, g0);
   int64_t g = g0;
   int32_t bad = 0;
+  const bool bs_pow2 = (a.bs & (a.bs - 1)) == 0;
+  const int bs_shift = __builtin_ctz((unsigned)a.bs);
 
   // per-lane LDS offsets (bytes) within a tile buffer
   const int krow0 = tok_of_row(n);                  // K row read for MFMA row n, subtile 0
@@ -141,7 +143,8 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
     const int32_t t0i = (int32_t)t0, t1i = (int32_t)t1;
     auto page_of = [&](int32_t tile) -> int32_t {
       const int32_t t = tile + (lane & 31);
-      return brow[(t < t1i ? t : t1i - 1) / a.bs];
+      const int32_t tc = t < t1i ? t : t1i - 1;
+      return brow[bs_pow2 ? (tc >> bs_shift) : tc / a.bs];
     };
     int32_t blk_next = page_of(t0i);
 
@@ -170,7 +173,8 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
         const bool page_ok = blk >= 0 && blk < a.num_blocks;
         // row index < num_blocks * block_size rows of 1152 B: below 2^31 for any pool that
         // fits in device memory
-        const uint32_t row = (uint32_t)blk * (uint32_t)a.bs + (uint32_t)(tc % a.bs);
+        const uint32_t slot = bs_pow2 ? (uint32_t)(tc & (a.bs - 1)) : (uint32_t)(tc % a.bs);
+        const uint32_t row = (uint32_t)blk * (uint32_t)a.bs + slot;
         if (page_ok)
           rowaddr = (uint64_t)Kc + (uint64_t)row * (kMlaDqk * 2);
         else
