@@ -32,6 +32,16 @@ CASES = [
     ("mla-32h", "mla-64h-b512", [1000, 2049, 5], dict(batch=3, num_q_heads=32)),
     ("mla-16h", "mla-64h-b512", [513, 70], dict(batch=2, num_q_heads=16)),
     ("mla-64h-bs16", "mla-64h-b512", [1000, 300], dict(batch=2, block_size=16)),
+    # requests of length 0 (every shard empty) beside non-empty ones, and a batch of only
+    # empty requests (no pages at all: every worker idle)
+    ("gqa-g16-empty-requests", "gqa-g16", [0, 100, 0], dict(batch=3)),
+    ("mla-64h-empty-requests", "mla-64h-b512", [0, 70, 0], dict(batch=3)),
+    ("mla-64h-all-empty", "mla-64h-b512", [0, 0], dict(batch=2)),
+    ("gqa-g16-all-empty", "gqa-g16", [0, 0], dict(batch=2)),
+    # block size 1 (a tile spans 32 pages) and a non-power-of-two block size
+    ("mla-64h-bs1", "mla-64h-b512", [200, 33], dict(batch=2, block_size=1)),
+    ("gqa-g16-bs24", "gqa-g16", [500, 49], dict(batch=2, block_size=24)),
+    ("mla-64h-bs48", "mla-64h-b512", [700, 97], dict(batch=2, block_size=48)),
 ]
 
 
