@@ -23,6 +23,14 @@ What it computes, and where each step comes from:
   section 2 says the same. The partial result is taken to be the softmax
   output over the slice together with its log-sum-exp of the scaled scores
   (natural log).
+* KV append (``append_token``). Decode makes one token per step and each
+  rank keeps only its own slice of the KV (naphjohn blog, section 4, the
+  decode bullet; Qiita token-range section). The new token of a request that
+  already holds L tokens has position L, so under the paged layout it is
+  stored at slot L % bs of page block_table[b, L // bs]; the shard that owns
+  it is the one whose range in the plan of the grown length L + 1 contains L
+  (always the last non-empty shard). Positions with no block-table entry or
+  entries outside the page pool are reported, not written.
 * Merge (``merge_lse``). The partial results are combined with online-softmax
   re-weighting and must give the full attention result (Qiita three-step
   paragraph; blog section 2). The re-weighting written out is the LSE merge:
@@ -213,3 +221,45 @@ def sharded_attention(kind, dtype, q, caches, block_table, seq_lens, num_shards,
                                          scale, head_dim_v, seqs)
     o, lse = merge_lse(part_o, part_lse)
     return bounds, part_o, part_lse, o, lse
+
+
+# ---------------------------------------------------------------- KV append
+
+def append_token(kind: str, caches, new_rows, block_table, seq_lens, block_size: int,
+                 num_shards: int):
+    """Store each request's newly decoded token in its page and name the owning shard.
+
+    kind "gqa": caches = (k_cache [N, Hkv, bs, D], v_cache [N, Hkv, bs, Dv]) and
+    new_rows = (new_k [B, Hkv, D], new_v [B, Hkv, Dv]); kind "mla": caches = (latent
+    [N, bs, D],) and new_rows = (new_latent [B, D],). seq_lens[b] = L_b tokens already
+    cached; the new token takes position L_b.
+
+    Returns (copies of the caches with the rows stored, owner int64 [B]): owner[b] is the
+    shard holding position L_b in plan_shards of L_b + 1 tokens; -1 when L_b < 0 or
+    L_b // bs is past the block table's row, -2 when the table entry is not a page in
+    [0, N). Nothing is stored for a request whose owner is negative. Requests are stored
+    in order of b, so if two of them name the same (page, slot) the later one stays.
+    """
+    out = tuple(np.array(c, copy=True) for c in caches)
+    table = np.asarray(block_table)
+    max_blocks = table.shape[1]
+    n_pages = out[0].shape[0]
+    owner = np.zeros(len(seq_lens), dtype=np.int64)
+    for b, L in enumerate(seq_lens):
+        L = int(L)
+        if L < 0 or L // block_size >= max_blocks:
+            owner[b] = -1
+            continue
+        page = int(table[b, L // block_size])
+        if page < 0 or page >= n_pages:
+            owner[b] = -2
+            continue
+        slot = L % block_size
+        ranges = plan_shards([L + 1], num_shards, block_size)[0]
+        owner[b] = next(s for s in range(num_shards) if ranges[s, 0] <= L < ranges[s, 1])
+        if kind == "mla":
+            out[0][page, slot] = new_rows[0][b]
+        else:
+            for i in range(2):
+                out[i][page, :, slot] = new_rows[i][b]
+    return out, owner

@@ -320,6 +320,115 @@ def check_bf16_upcast():
     assert math.copysign(1.0, got[5]) == -1.0
 
 
+# ------------------------------------------------------------------ KV append
+
+def check_append_example():
+    """bs 4, table rows [2, 0, 3] and [1, 3, 0]: positions placed by hand."""
+    bs, N, Hkv, D = 4, 4, 2, 3
+    k = np.zeros((N, Hkv, bs, D))
+    v = np.zeros((N, Hkv, bs, D))
+    table = np.array([[2, 0, 3], [1, 3, 0]], dtype=np.int32)
+    nk = np.arange(2 * Hkv * D, dtype=float).reshape(2, Hkv, D) + 1
+    nv = -nk
+    # request 0 holds 5 tokens: the sixth (position 5) goes to page 0, slot 1;
+    # request 1 holds 8: position 8 is the first slot of its third page, 0.
+    (k2, v2), owner = O.append_token("gqa", (k, v), (nk, nv), table, [5, 8], bs, 2)
+    hit = sorted(map(tuple, np.argwhere(k2[..., 0] != 0).tolist()))
+    assert hit == [(0, 0, 0), (0, 0, 1), (0, 1, 0), (0, 1, 1)], hit
+    assert k2[0, :, 1].tolist() == nk[0].tolist() and v2[0, :, 1].tolist() == nv[0].tolist()
+    assert k2[0, :, 0].tolist() == nk[1].tolist() and v2[0, :, 0].tolist() == nv[1].tolist()
+    # 6 tokens on 2 shards of whole pages: [0, 4) and [4, 6) -> position 5 on shard 1;
+    # 9 tokens: 3 pages, 2 per shard: [0, 8) and [8, 9) -> position 8 on shard 1.
+    assert owner.tolist() == [1, 1]
+    # A first token always lands on shard 0, page table[b, 0], slot 0.
+    lat = np.zeros((N, bs, D))
+    (lat2,), owner = O.append_token("mla", (lat,), (np.full((2, D), 7.0),), table, [0, 0], bs, 4)
+    assert owner.tolist() == [0, 0]
+    assert sorted(map(tuple, np.argwhere(lat2[..., 0] != 0).tolist())) == [(1, 0), (2, 0)]
+    # Qiita's 200K tokens on 4 GPUs (0-50K, ..., 150K-200K): the token that completes the
+    # 200K context is stored on the fourth GPU; token 100000 of a 100001-token request is on
+    # the last shard of that request's own plan.
+    big = np.zeros((1, 12500), dtype=np.int32)
+    one = np.zeros((1, 1, D))
+    _, owner = O.append_token("mla", (one[:, :1].repeat(16, 1),), (np.ones((1, D)),), big,
+                              [199_999], 16, 4)
+    assert owner.tolist() == [3]
+    _, owner = O.append_token("mla", (one[:, :1].repeat(16, 1),), (np.ones((1, D)),), big,
+                              [100_000], 16, 4)
+    assert owner.tolist() == [3]
+
+
+def check_append_replay():
+    """Decoding token by token from empty pages rebuilds each request's dense history:
+    the paged reader returns exactly the rows appended, pages outside the requests' tables
+    stay untouched, and attention over the grown cache equals brute force on the history."""
+    rng = np.random.default_rng(11)
+    bs, N, Hkv, D, Dv, max_blocks = 4, 16, 2, 5, 3, 4
+    lens = [13, 0, 7]
+    B = len(lens)
+    table = rng.permutation(N)[:B * max_blocks].reshape(B, max_blocks).astype(np.int32)
+    spare = sorted(set(range(N)) - set(table.ravel().tolist()))
+    k = np.full((N, Hkv, bs, D), np.nan)
+    v = np.full((N, Hkv, bs, Dv), np.nan)
+    lat = np.full((N, bs, D), np.nan)
+    hist_k = rng.standard_normal((B, max(lens), Hkv, D))
+    hist_v = rng.standard_normal((B, max(lens), Hkv, Dv))
+    for t in range(max(lens)):
+        cur = [t if t < L else max_blocks * bs for L in lens]  # finished requests fall off
+        (k, v), owner = O.append_token("gqa", (k, v), (hist_k[:, t], hist_v[:, t]), table, cur,
+                                       bs, 3)
+        (lat,), _ = O.append_token("mla", (lat,), (hist_k[:, t, 0],), table, cur, bs, 3)
+        assert [o >= 0 for o in owner.tolist()] == [t < L for L in lens]
+    for b, L in enumerate(lens):
+        for g in range(Hkv):
+            assert np.array_equal(O.gather_gqa(k, table, b, g, 0, L, bs), hist_k[b, :L, g])
+            assert np.array_equal(O.gather_gqa(v, table, b, g, 0, L, bs), hist_v[b, :L, g])
+        assert np.array_equal(O.gather_mla(lat, table, b, 0, L, bs), hist_k[b, :L, 0])
+    assert np.isnan(k[spare]).all() and np.isnan(v[spare]).all() and np.isnan(lat[spare]).all()
+    q = rng.standard_normal((Hkv, D))
+    o, lse = O.attention(q, O.gather_gqa(k, table, 0, 1, 0, lens[0], bs),
+                         O.gather_gqa(v, table, 0, 1, 0, lens[0], bs), 0.3)
+    bo, blse = _brute_attention(q, hist_k[0, :lens[0], 1], hist_v[0, :lens[0], 1], 0.3)
+    assert np.allclose(o, bo, rtol=1e-12, atol=1e-13) and np.allclose(lse, blse, rtol=1e-13)
+
+
+def check_append_owner_brute(rng=None):
+    """The owner is the shard whose brute-force range holds position L of an (L+1)-token
+    request, and it is the last non-empty shard of that plan."""
+    rng = rng or np.random.default_rng(12)
+    cases = [(0, 1, 1), (0, 4, 16), (15, 4, 16), (16, 4, 16), (63, 8, 16), (64, 8, 16)]
+    cases += [(int(rng.integers(0, 4000)), int(rng.integers(1, 17)),
+               int(rng.choice([1, 3, 16, 64]))) for _ in range(200)]
+    for L, S, bs in cases:
+        pages = L // bs + 1
+        table = np.zeros((1, pages), dtype=np.int32)
+        _, owner = O.append_token("mla", (np.zeros((1, bs, 1)),), (np.ones((1, 1)),), table,
+                                  [L], bs, S)
+        ranges = _plan_brute(L + 1, S, bs)
+        want = [s for s, (a, e) in enumerate(ranges) if a <= L < e]
+        last = max(s for s, (a, e) in enumerate(ranges) if e > a)
+        assert owner.tolist() == want == [last], (L, S, bs, owner, ranges)
+
+
+def check_append_rejects():
+    """Positions past the table row, negative lengths and page ids outside the pool store
+    nothing and are reported with -1 / -2."""
+    rng = np.random.default_rng(13)
+    bs, N, Hkv, D = 4, 6, 1, 2
+    k = rng.standard_normal((N, Hkv, bs, D))
+    v = rng.standard_normal((N, Hkv, bs, D))
+    table = np.array([[0, 1], [2, -1], [3, 6], [4, 5], [5, 4]], dtype=np.int32)
+    new = (np.full((5, Hkv, D), 9.0), np.full((5, Hkv, D), 8.0))
+    (k2, v2), owner = O.append_token("gqa", (k, v), new, table, [8, 4, -3, 11, 2], bs, 2)
+    assert owner.tolist() == [-1, -2, -1, -1, 0]
+    changed = sorted(map(tuple, np.argwhere((k2 != k).any(axis=-1)).tolist()))
+    assert changed == [(5, 0, 2)], changed
+    assert np.array_equal(k2[5, 0, 2], [9.0, 9.0]) and np.array_equal(v2[5, 0, 2], [8.0, 8.0])
+    (k3, _), owner = O.append_token("gqa", (k, v), new, table, [0, 5, 4, 8, 8], bs, 2)
+    assert owner.tolist() == [0, -2, -2, -1, -1]
+    assert sorted(map(tuple, np.argwhere((k3 != k).any(axis=-1)).tolist())) == [(0, 0, 0)]
+
+
 ALL_CHECKS = [
     check_bf16_upcast,
     check_plan_golden,
@@ -336,4 +445,8 @@ ALL_CHECKS = [
     check_gqa_head_groups,
     check_mla_value_is_latent_prefix,
     check_sharded_equals_full,
+    check_append_example,
+    check_append_replay,
+    check_append_owner_brute,
+    check_append_rejects,
 ]

@@ -18,6 +18,7 @@ _gm = O.gather_mla
 _gf = O._gather_fast
 _partial = O.partial_attention
 _up = O.bf16_bits_to_f64
+_append = O.append_token
 
 
 def m_attn_no_scale(q, k, v, scale):
@@ -146,6 +147,50 @@ def m_upcast_shift15(bits):
     return u.view(np.float32).astype(np.float64)
 
 
+def m_append_slot_page_swapped(kind, caches, new_rows, table, seq_lens, bs, S):
+    out = tuple(np.array(c, copy=True) for c in caches)
+    _, owner = _append(kind, caches, new_rows, table, seq_lens, bs, S)
+    for b, L in enumerate(seq_lens):
+        if owner[b] < 0:
+            continue
+        page, slot = int(table[b, L % bs % table.shape[1]]), min(L // bs, bs - 1)
+        if kind == "mla":
+            out[0][page, slot] = new_rows[0][b]
+        else:
+            out[0][page, :, slot], out[1][page, :, slot] = new_rows[0][b], new_rows[1][b]
+    return out, owner
+
+
+def m_append_next_position(kind, caches, new_rows, table, seq_lens, bs, S):
+    return _append(kind, caches, new_rows, table, [int(L) + 1 for L in seq_lens], bs, S)
+
+
+def m_append_owner_from_old_length(kind, caches, new_rows, table, seq_lens, bs, S):
+    out, owner = _append(kind, caches, new_rows, table, seq_lens, bs, S)
+    for b, L in enumerate(seq_lens):
+        if owner[b] >= 0:
+            k = -(-(-(-int(L) // bs)) // S)
+            owner[b] = 0 if k == 0 else min(S - 1, int(L) // (k * bs))
+    return out, owner
+
+
+def m_append_owner_last_shard(kind, caches, new_rows, table, seq_lens, bs, S):
+    out, owner = _append(kind, caches, new_rows, table, seq_lens, bs, S)
+    return out, np.where(owner >= 0, S - 1, owner)
+
+
+def m_append_no_page_check(kind, caches, new_rows, table, seq_lens, bs, S):
+    n = caches[0].shape[0]
+    wrapped = np.where((np.asarray(table) < 0) | (np.asarray(table) >= n), 0, table)
+    return _append(kind, caches, new_rows, wrapped, seq_lens, bs, S)
+
+
+def m_append_k_gets_v(kind, caches, new_rows, table, seq_lens, bs, S):
+    if kind != "gqa" or new_rows[0].shape != new_rows[1].shape:
+        return _append(kind, caches, new_rows, table, seq_lens, bs, S)
+    return _append(kind, caches, (new_rows[1], new_rows[0]), table, seq_lens, bs, S)
+
+
 MUTANTS = [
     ("attention", m_attn_no_scale),
     ("attention", m_attn_log2),
@@ -165,6 +210,12 @@ MUTANTS = [
     ("partial_attention", m_partial_interleaved_heads),
     ("partial_attention", m_partial_value_suffix),
     ("bf16_bits_to_f64", m_upcast_shift15),
+    ("append_token", m_append_slot_page_swapped),
+    ("append_token", m_append_next_position),
+    ("append_token", m_append_owner_from_old_length),
+    ("append_token", m_append_owner_last_shard),
+    ("append_token", m_append_no_page_check),
+    ("append_token", m_append_k_gets_v),
 ]
 
 
