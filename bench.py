@@ -197,6 +197,46 @@ def cpu_baseline(wl, inp, bounds_np, seconds):
 
 # ------------------------------------------------------------------ main
 
+def time_append(wl, sh, inp, k_cache, v_cache, dev, n):
+    """Time dcp_append_kv storing one new row per request (after the attention timing, so the
+    attention inputs are untouched while they are measured). Each request rewrites the slot
+    of its last cached token, which its block table always covers."""
+    import torch
+    import sequence_sharded_kv_amd as dcp
+    from workloads import make_new_rows
+    rows = make_new_rows(wl)
+    dev_rows = {}
+    for k, a in rows.items():
+        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+        dev_rows[k] = t.view(torch.bfloat16) if a.dtype == np.uint16 else t
+    nk = dev_rows["new_latent"] if wl.kind == "mla" else dev_rows["new_k"]
+    nv = None if wl.kind == "mla" else dev_rows["new_v"]
+    pos = torch.clamp(inp["seq_lens"] - 1, min=0).to(torch.int32)
+    owner = torch.empty(wl.batch, dtype=torch.int32, device=dev)
+
+    def call():
+        dcp.dcp_append_kv(sh, pos, nk, nv, inp["block_table"], k_cache, v_cache, owner)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    assert int(owner.min()) >= 0
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / n
+    esz = 2 if wl.dtype == "bf16" else 4
+    heads = 1 if wl.kind == "mla" else wl.num_kv_heads
+    row = heads * (wl.head_dim_qk + (0 if wl.kind == "mla" else wl.head_dim_v)) * esz
+    nbytes = wl.batch * (2 * row + 3 * 4)   # new rows read, cache rows written, len/table/owner
+    return {"us_per_launch": round(us, 3), "launches": n, "algorithmic_bytes": nbytes,
+            "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "bound": "launch latency (one row per request)"}
+
+
 def main():
     args = parse_args()
     from workloads import make_device_inputs, workload
@@ -277,6 +317,7 @@ def main():
                 "traffic": None if traffic is None else int(traffic["traffic_bytes_per_launch"]),
                 "kernel": KERNEL_NAMES[family], "kernel_avg_ms": round(kern_avg_ms, 4),
                 "algorithmic_bytes_per_launch": int(bm["partial_kernel"])}
+    append = time_append(wl, sh, inp, k_cache, v_cache, dev, max(K, 20))
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -300,6 +341,7 @@ def main():
                    "parallelism": "all shards on one GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "append_kv": append,
     }
     print(json.dumps(line), flush=True)
     return 0

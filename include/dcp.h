@@ -199,6 +199,37 @@ dcp_status dcp_debug_gather_shard(const dcp_attn_shape* shape, const void* cache
                                   void* stream);
 
 /*
+ * dcp_append_kv -- the step that precedes attention on every decode step: store the K/V (GQA)
+ * or latent (MLA) row of the token each request just produced. Decode emits one token per
+ * request per step and, under DCP, only the rank owning the token's range keeps its KV
+ * (naphjohn blog "Inference Systems Infrastructure Notes (7)", section 4, decode bullet;
+ * Qiita article on vLLM -dcp, section on assigning token ranges to GPUs). A request that
+ * holds L_b tokens stores its new token at position L_b: slot L_b % block_size of page
+ * block_table[b * max_blocks_per_seq + L_b / block_size] (paged KV, as for attention).
+ *   shape:       as for attention; batch, num_kv_heads, head_dim_qk, head_dim_v, block_size,
+ *                max_blocks_per_seq, num_blocks, num_shards, dtype and kv_kind are used.
+ *   seq_lens:    device int32 [B]: L_b, tokens cached before this step (the new position).
+ *   new_k:       device, GQA [B][Hkv][Dqk]; MLA [B][Dqk] (the latent row, rope part included).
+ *   new_v:       device, GQA [B][Hkv][Dv]; MLA must be NULL.
+ *   block_table: device int32 [B][max_blocks_per_seq].
+ *   k_cache, v_cache: device caches in the attention layouts, updated in place (v_cache NULL
+ *                for MLA). Only the B addressed rows (per KV head) are written.
+ *   owner:       device int32 [B] or NULL. owner[b] = the shard whose range in the canonical
+ *                plan of L_b + 1 tokens (dcp_plan_shards) holds position L_b, i.e. the last
+ *                non-empty shard; -1 if L_b < 0 or L_b / block_size >= max_blocks_per_seq;
+ *                -2 if the table entry is outside [0, num_blocks). Nothing is stored for a
+ *                request with a negative owner.
+ * Row bytes (Dqk, and Dv for GQA, times the element size) must be multiples of 16. The new
+ * rows must not overlap the caches, and two requests must not address the same (page, slot)
+ * in one call (which of them is kept is then unspecified). Asynchronous on `stream`.
+ * Errors: DCP_ERR_NULL, DCP_ERR_ALIGN, DCP_ERR_SHAPE (also: MLA with new_v or v_cache),
+ * DCP_ERR_UNSUPPORTED (row bytes), DCP_ERR_DEVICE.
+ */
+dcp_status dcp_append_kv(const dcp_attn_shape* shape, const int32_t* seq_lens, const void* new_k,
+                         const void* new_v, const int32_t* block_table, void* k_cache,
+                         void* v_cache, int32_t* owner, void* stream);
+
+/*
  * Kernel timing for benchmarks (no effect on results). dcp_kernel_timing_begin(n) creates n
  * pairs of HIP events; while timing is on for the calling thread, each of the next n
  * dcp_decode_attn / dcp_decode_attn_partial calls records one pair around its

@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     DcpError,
     dcp_abi_version,
+    dcp_append_kv,
     dcp_attn_shape,
     dcp_debug_gather_shard,
     dcp_decode_attn,

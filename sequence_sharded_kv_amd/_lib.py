@@ -34,7 +34,7 @@ EXPORTS = (
     "dcp_abi_version", "dcp_status_string", "dcp_last_error", "dcp_plan_shards",
     "dcp_plan_shards_device", "dcp_workspace_bytes", "dcp_decode_attn_partial", "dcp_merge_lse",
     "dcp_decode_attn", "dcp_read_device_flags", "dcp_debug_gather_shard",
-    "dcp_kernel_timing_begin", "dcp_kernel_timing_end",
+    "dcp_kernel_timing_begin", "dcp_kernel_timing_end", "dcp_append_kv",
 )
 
 
@@ -83,6 +83,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "dcp_debug_gather_shard": (I32, [SH, P, P, P, I32, I32, I32, P, I32, P]),
         "dcp_kernel_timing_begin": (I32, [I32]),
         "dcp_kernel_timing_end": (I32, [ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_float)]),
+        "dcp_append_kv": (I32, [SH, P, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -194,6 +195,15 @@ def dcp_debug_gather_shard(shape: dcp_attn_shape, cache, block_table, bounds, b:
     _check(load().dcp_debug_gather_shard(
         ctypes.byref(shape), _ptr(cache), _ptr(block_table), _ptr(bounds), b, s, kv_head,
         _ptr(dst), max_rows, _stream(cache)))
+
+
+def dcp_append_kv(shape: dcp_attn_shape, seq_lens, new_k, new_v, block_table, k_cache, v_cache,
+                  owner=None) -> None:
+    """Store each request's new row at position seq_lens[b]; owner (int32 [B]) gets the
+    owning shard, -1 / -2 for a position without a page / a page outside the pool."""
+    _check(load().dcp_append_kv(
+        ctypes.byref(shape), _ptr(seq_lens), _ptr(new_k), _ptr(new_v), _ptr(block_table),
+        _ptr(k_cache), _ptr(v_cache), _ptr(owner), _stream(k_cache)))
 
 
 def dcp_kernel_timing_begin(max_launches: int) -> None:

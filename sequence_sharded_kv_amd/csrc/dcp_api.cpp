@@ -371,6 +371,29 @@ dcp_status dcp_debug_gather_shard(const dcp_attn_shape* shape, const void* cache
   return ok();
 }
 
+dcp_status dcp_append_kv(const dcp_attn_shape* shape, const int32_t* seq_lens,
+                         const void* new_k, const void* new_v, const int32_t* block_table,
+                         void* k_cache, void* v_cache, int32_t* owner, void* stream) {
+  dcp_status st = check_shape(shape);
+  if (st != DCP_OK) return st;
+  if (!seq_lens || !new_k || !block_table || !k_cache)
+    return fail(DCP_ERR_NULL, "seq_lens, new_k, block_table and k_cache must be non-NULL");
+  const bool gqa = shape->kv_kind == DCP_KV_GQA;
+  if (gqa && (!new_v || !v_cache)) return fail(DCP_ERR_NULL, "GQA needs new_v and v_cache");
+  if (!gqa && (new_v || v_cache))
+    return fail(DCP_ERR_SHAPE, "MLA stores one latent row; new_v and v_cache must be NULL");
+  if (!aligned16(new_k) || !aligned16(k_cache) || (gqa && (!aligned16(new_v) || !aligned16(v_cache))))
+    return fail(DCP_ERR_ALIGN, "new rows and caches must be 16-byte aligned");
+  const int32_t esize = shape->dtype == DCP_F32 ? 4 : 2;
+  if ((shape->head_dim_qk * esize) % 16 != 0 || (gqa && (shape->head_dim_v * esize) % 16 != 0))
+    return fail(DCP_ERR_UNSUPPORTED, "cache rows must be whole 16-byte chunks (head_dim %d/%d)",
+                shape->head_dim_qk, shape->head_dim_v);
+  hipError_t e = dcp::launch_append_kv(*shape, seq_lens, new_k, new_v, block_table, k_cache,
+                                       v_cache, owner, as_stream(stream));
+  if (e != hipSuccess) return device_fail(e, "append launch");
+  return ok();
+}
+
 dcp_status dcp_kernel_timing_begin(int32_t max_launches) {
   if (max_launches < 1) return fail(DCP_ERR_SHAPE, "max_launches must be >= 1");
   destroy_timing_events();

@@ -84,6 +84,9 @@ hipError_t launch_debug_gather(const dcp_attn_shape& sh, const void* cache,
                                const int32_t* block_table, const int32_t* bounds, int32_t b,
                                int32_t s, int32_t kv_head, void* dst, int32_t max_rows,
                                hipStream_t stream);
+hipError_t launch_append_kv(const dcp_attn_shape& sh, const int32_t* seq_lens,
+                            const void* new_k, const void* new_v, const int32_t* block_table,
+                            void* k_cache, void* v_cache, int32_t* owner, hipStream_t stream);
 
 // Partial-attention kernels. `workers` returns the P the launcher will use (<= max_workers).
 int32_t gqa_valu_workers(int device, int32_t max_workers);

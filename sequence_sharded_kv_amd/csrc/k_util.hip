@@ -291,4 +291,63 @@ hipError_t launch_debug_gather(const dcp_attn_shape& sh, const void* cache,
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------- KV append
+
+// One workgroup per request stores the token it decoded this step. A request holding L tokens
+// writes position L: slot L % bs of page block_table[b][L / bs]. Its owner is the shard whose
+// range in the plan of L + 1 tokens contains L: with p = L / bs that plan has p + 1 pages and
+// k = ceil((p + 1) / S) pages per shard, so the owner is p / k. Rows move as 16-byte chunks:
+// kc (and vc) chunks per head, Hkv heads (1 for the MLA latent cache, vc = 0).
+constexpr int32_t kAppendThreads = 128;
+
+__global__ void __launch_bounds__(kAppendThreads)
+append_kv_kernel(const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_table,
+                 const i32x4* __restrict__ new_k, const i32x4* __restrict__ new_v,
+                 i32x4* __restrict__ k_cache, i32x4* __restrict__ v_cache,
+                 int32_t* __restrict__ owner, int32_t Hkv, int32_t kc, int32_t vc, int32_t bs,
+                 int32_t max_blocks, int32_t num_blocks, int32_t S) {
+  const int32_t b = blockIdx.x;
+  const int32_t L = seq_lens[b];
+  const int32_t p = L >= 0 ? L / bs : 0;
+  int32_t who = -1;
+  int32_t blk = 0;
+  if (L >= 0 && p < max_blocks) {
+    blk = block_table[(int64_t)b * max_blocks + p];
+    if (blk < 0 || blk >= num_blocks) {
+      who = -2;
+    } else {
+      const int64_t per_shard = ((int64_t)p + S) / S;
+      who = (int32_t)(p / per_shard);
+    }
+  }
+  if (owner && threadIdx.x == 0) owner[b] = who;
+  if (who < 0) return;
+  const int32_t slot = L - p * bs;
+  const int32_t per_head = kc + vc;
+  for (int32_t i = threadIdx.x; i < Hkv * per_head; i += kAppendThreads) {
+    const int32_t h = i / per_head, j = i - h * per_head;
+    const int64_t row = ((int64_t)blk * Hkv + h) * bs + slot;
+    const int64_t src = (int64_t)b * Hkv + h;
+    if (j < kc)
+      k_cache[row * kc + j] = new_k[src * kc + j];
+    else
+      v_cache[row * vc + (j - kc)] = new_v[src * vc + (j - kc)];
+  }
+}
+
+hipError_t launch_append_kv(const dcp_attn_shape& sh, const int32_t* seq_lens,
+                            const void* new_k, const void* new_v, const int32_t* block_table,
+                            void* k_cache, void* v_cache, int32_t* owner, hipStream_t stream) {
+  const int32_t esize = sh.dtype == DCP_F32 ? 4 : 2;
+  const bool gqa = sh.kv_kind == DCP_KV_GQA;
+  const int32_t kc = sh.head_dim_qk * esize / 16;
+  const int32_t vc = gqa ? sh.head_dim_v * esize / 16 : 0;
+  hipLaunchKernelGGL(append_kv_kernel, dim3(sh.batch), dim3(kAppendThreads), 0, stream, seq_lens,
+                     block_table, (const i32x4*)new_k, (const i32x4*)new_v, (i32x4*)k_cache,
+                     (i32x4*)v_cache, owner, gqa ? sh.num_kv_heads : 1, kc, vc, sh.block_size,
+                     sh.max_blocks_per_seq, sh.num_blocks, sh.num_shards);
+  return hipGetLastError();
+}
+
 }  // namespace dcp

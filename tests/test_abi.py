@@ -24,7 +24,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = dcp.load()
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(dcp.EXPORTS) == names
@@ -156,3 +156,31 @@ def test_merge_and_fused_error_paths():
     assert lib.dcp_read_device_flags(None, None, None) == dcp.DCP_ERR_NULL
     assert lib.dcp_kernel_timing_begin(0) == dcp.DCP_ERR_SHAPE
     assert lib.dcp_kernel_timing_end(None, None) == dcp.DCP_ERR_NULL
+
+
+def test_append_error_paths_return_before_device_work():
+    lib = dcp.load()
+    A = 0x10000
+
+    def call(sh, lens=A, nk=A, nv=None, bt=A, kc=A, vc=None, owner=None):
+        return lib.dcp_append_kv(ctypes.byref(sh), lens, nk, nv, bt, kc, vc, owner, None)
+
+    mla = _shape()
+    assert call(mla, lens=None) == dcp.DCP_ERR_NULL
+    assert call(mla, nk=None) == dcp.DCP_ERR_NULL
+    assert call(mla, bt=None) == dcp.DCP_ERR_NULL
+    assert call(mla, kc=None) == dcp.DCP_ERR_NULL
+    assert call(mla, nv=A) == dcp.DCP_ERR_SHAPE
+    assert call(mla, vc=A) == dcp.DCP_ERR_SHAPE
+    assert call(mla, nk=A + 8) == dcp.DCP_ERR_ALIGN
+    assert call(mla, kc=A + 2) == dcp.DCP_ERR_ALIGN
+    assert call(_shape(batch=0)) == dcp.DCP_ERR_SHAPE
+    # 36 bf16 dims = 72 bytes: not whole 16-byte chunks
+    assert call(_shape(head_dim_qk=36, head_dim_v=32)) == dcp.DCP_ERR_UNSUPPORTED
+    gqa = _shape(kind="gqa", num_q_heads=8, num_kv_heads=2, head_dim_qk=64, head_dim_v=64)
+    assert call(gqa) == dcp.DCP_ERR_NULL
+    assert "new_v" in dcp.dcp_last_error()
+    assert call(gqa, nv=A) == dcp.DCP_ERR_NULL
+    assert call(gqa, nv=A + 4, vc=A) == dcp.DCP_ERR_ALIGN
+    gqa_odd = _shape(kind="gqa", num_q_heads=8, num_kv_heads=2, head_dim_qk=4, head_dim_v=4)
+    assert call(gqa_odd, nv=A, vc=A) == dcp.DCP_ERR_UNSUPPORTED

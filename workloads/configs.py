@@ -231,6 +231,28 @@ def make_host_inputs(wl: Workload, seed: Optional[int] = None, lengths=None, max
     return out
 
 
+def make_new_rows(wl: Workload, seed: Optional[int] = None, batch: Optional[int] = None):
+    """Rows of the token each request decodes this step, drawn like the cache rows.
+
+    GQA: {"new_k": [B, Hkv, Dqk], "new_v": [B, Hkv, Dv]}; MLA: {"new_latent": [B, Dqk]}.
+    bf16 arrays are uint16 bit patterns, f32 arrays float32.
+    """
+    B = wl.batch if batch is None else batch
+    rng = np.random.default_rng(np.random.SeedSequence(2000 + wl.seed_index if seed is None
+                                                       else seed))
+    std = _std_vector(wl)
+    if wl.kind == KIND_MLA:
+        rows = {"new_latent": rng.standard_normal((B, wl.head_dim_qk), dtype=np.float32) * std}
+    else:
+        rows = {"new_k": rng.standard_normal((B, wl.num_kv_heads, wl.head_dim_qk),
+                                             dtype=np.float32) * std,
+                "new_v": rng.standard_normal((B, wl.num_kv_heads, wl.head_dim_v),
+                                             dtype=np.float32) * std[:wl.head_dim_v]}
+    if wl.dtype == "bf16":
+        rows = {k: bf16_bits_from_f32(v) for k, v in rows.items()}
+    return rows
+
+
 def _plant_host(wl: Workload, inp: dict, ss) -> None:
     rng = np.random.default_rng(ss)
     is_bf16 = wl.dtype == "bf16"
