@@ -23,6 +23,15 @@ What it computes, and where each step comes from:
   section 2 says the same. The partial result is taken to be the softmax
   output over the slice together with its log-sum-exp of the scaled scores
   (natural log).
+* Several query tokens per request (``partial_attention_multi``). Both pages
+  list speculative decoding / MTP as work that DCP is to be combined with
+  (Qiita, section "実務でどう見るか"; naphjohn blog, section 5). Such a step
+  scores q_len new tokens at once. The reading taken here: they are the
+  request's q_len newest positions L - q_len .. L - 1 (L = the end of the
+  ranges that cover the request), their KV is already in the cache, and token
+  j attends to every position up to and including its own (causal order).
+  Each shard's partial is then the softmax over the shard's tokens that the
+  row may see, and the same LSE merge gives the causal attention result.
 * KV append (``append_token``). Decode makes one token per step and each
   rank keeps only its own slice of the KV (naphjohn blog, section 4, the
   decode bullet; Qiita token-range section). The new token of a request that
@@ -222,6 +231,59 @@ def sharded_attention(kind, dtype, q, caches, block_table, seq_lens, num_shards,
     o, lse = merge_lse(part_o, part_lse)
     return bounds, part_o, part_lse, o, lse
 
+
+# ---------------------------------------------------------------- several query tokens
+
+def partial_attention_multi(kind: str, dtype: str, q, caches, block_table, bounds,
+                            block_size: int, scale: float, head_dim_v: int, seqs=None):
+    """Per-shard partials for q_len query tokens per request, with causal visibility.
+
+    q [B, q_len, Hq, Dqk]; bounds [B, S, 2]. With L_b the largest end among request b's
+    ranges, query token j sits at position L_b - q_len + j and sees token t only when
+    t <= L_b - q_len + j. Returns part_o [B, S, q_len, Hq, Dv] and part_lse [B, S, q_len, Hq]
+    (a row that sees nothing in a shard gets O = 0, LSE = -inf; rows of sequences not in
+    `seqs` stay NaN).
+    """
+    B, q_len, Hq = q.shape[0], q.shape[1], q.shape[2]
+    S = bounds.shape[1]
+    part_o = np.full((B, S, q_len, Hq, head_dim_v), np.nan)
+    part_lse = np.full((B, S, q_len, Hq), np.nan)
+    for b in (range(B) if seqs is None else seqs):
+        L = int(np.max(bounds[b, :, 1])) if S else 0
+        for s in range(S):
+            start, end = int(bounds[b, s, 0]), int(bounds[b, s, 1])
+            for j in range(q_len):
+                last = min(end, L - q_len + j + 1)   # exclusive end of the visible part
+                stop = max(start, last)
+                if kind == "mla":
+                    rows = as_f64(_gather_fast(caches[0], block_table, b, start, stop,
+                                               block_size), dtype)
+                    o, lse = attention(as_f64(q[b, j], dtype), rows, rows[:, :head_dim_v], scale)
+                    part_o[b, s, j], part_lse[b, s, j] = o, lse
+                else:
+                    k_cache, v_cache = caches
+                    G = Hq // k_cache.shape[1]
+                    for g in range(k_cache.shape[1]):
+                        k = as_f64(_gather_fast(k_cache, block_table, b, start, stop,
+                                                block_size, g), dtype)
+                        v = as_f64(_gather_fast(v_cache, block_table, b, start, stop,
+                                                block_size, g), dtype)
+                        o, lse = attention(as_f64(q[b, j, g * G:(g + 1) * G], dtype), k, v, scale)
+                        part_o[b, s, j, g * G:(g + 1) * G] = o
+                        part_lse[b, s, j, g * G:(g + 1) * G] = lse
+    return part_o, part_lse
+
+
+def sharded_attention_multi(kind, dtype, q, caches, block_table, seq_lens, num_shards,
+                            block_size, scale, head_dim_v, seqs=None):
+    """Plan of seq_lens, causal partials, merge: (bounds, part_o, part_lse, O, LSE) with
+    O [B, q_len, Hq, Dv] and LSE [B, q_len, Hq]."""
+    bounds = plan_shards(seq_lens, num_shards, block_size)
+    part_o, part_lse = partial_attention_multi(kind, dtype, q, caches, block_table, bounds,
+                                               block_size, scale, head_dim_v, seqs)
+    B, S, T, H, Dv = part_o.shape
+    o, lse = merge_lse(part_o.reshape(B, S, T * H, Dv), part_lse.reshape(B, S, T * H))
+    return bounds, part_o, part_lse, o.reshape(B, T, H, Dv), lse.reshape(B, T, H)
 
 # ---------------------------------------------------------------- KV append
 

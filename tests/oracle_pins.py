@@ -320,6 +320,87 @@ def check_bf16_upcast():
     assert math.copysign(1.0, got[5]) == -1.0
 
 
+# ------------------------------------------------------------------ several query tokens
+
+def check_multi_hand_example():
+    """Zero keys make every score 0, so a row's output is the mean of the values it may see:
+    L = 3, two query tokens at positions 1 and 2, shards [0, 2) and [2, 3) (block size 1)."""
+    v = np.array([[1.0, 0.0], [3.0, 6.0], [8.0, -3.0]])
+    cache = np.zeros((3, 1, 4))
+    cache[:, 0, :2] = v
+    cache[:, 0, 2:] = 0.0
+    q = np.ones((1, 2, 1, 4))
+    q[..., :2] = 0.0                       # q . k = 0 for every row and token
+    table = np.array([[2, 0, 1]], dtype=np.int32)
+    paged = cache[[1, 2, 0]]               # page table[0, t] holds token t's row
+    bounds = np.array([[[0, 2], [2, 3]]])
+    po, pl = O.partial_attention_multi("mla", "f32", q.astype(np.float32),
+                                       (paged.astype(np.float32),), table, bounds, 1, 0.5, 2)
+    # token 0 (position 1) sees tokens 0, 1 in shard 0 and nothing in shard 1
+    assert np.allclose(po[0, 0, 0, 0], [2.0, 3.0]) and math.isclose(pl[0, 0, 0, 0], math.log(2))
+    assert np.all(po[0, 1, 0, 0] == 0.0) and np.isneginf(pl[0, 1, 0, 0])
+    # token 1 (position 2) sees all three
+    assert np.allclose(po[0, 1, 1, 0], [8.0, -3.0]) and math.isclose(pl[0, 1, 1, 0], 0.0,
+                                                                     abs_tol=1e-15)
+    o, lse = O.merge_lse(po.reshape(1, 2, 2, 2), pl.reshape(1, 2, 2))
+    assert np.allclose(o[0, 1], [4.0, 1.0]) and math.isclose(lse[0, 1], math.log(3))
+    assert np.allclose(o[0, 0], [2.0, 3.0])
+
+
+def check_multi_rows_are_prefix_decodes():
+    """Row j of a q_len-token step equals a one-token decode whose context ends at its own
+    position, for every plan and both cache kinds; q_len = 1 is the one-token path."""
+    from workloads import workload, make_host_inputs
+    rng = np.random.default_rng(21)
+    for name, lens, S, T in (("gqa-tiny", [40, 5], 3, 3), ("gqa-tiny", [17, 2], 2, 4)):
+        wl = workload(name).replace(lengths=tuple(lens))
+        inp = make_host_inputs(wl, lengths=lens)
+        caches = (inp["k_cache"], inp["v_cache"])
+        q = rng.standard_normal((wl.batch, T, wl.num_q_heads, wl.head_dim_qk)).astype(np.float32)
+        _, _, _, o, lse = O.sharded_attention_multi("gqa", "f32", q, caches, inp["block_table"],
+                                                    lens, S, wl.block_size, 0.2, wl.head_dim_v)
+        for j in range(T):
+            pre = [max(0, L - T + j + 1) for L in lens]
+            fo, fl = O.full_attention("gqa", "f32", q[:, j], caches, inp["block_table"], pre,
+                                      wl.block_size, 0.2, wl.head_dim_v)
+            seen = np.array([p > 0 for p in pre])
+            assert np.allclose(o[seen, j], fo[seen], rtol=1e-11, atol=1e-12)
+            assert np.allclose(lse[seen, j], fl[seen], rtol=1e-12)
+            assert np.all(o[~seen, j] == 0.0) and np.all(np.isneginf(lse[~seen, j]))
+        one = O.partial_attention_multi("gqa", "f32", q[:, :1], caches, inp["block_table"],
+                                        O.plan_shards(lens, S, wl.block_size), wl.block_size,
+                                        0.2, wl.head_dim_v)
+        ref = O.partial_attention("gqa", "f32", q[:, 0], caches, inp["block_table"],
+                                  O.plan_shards(lens, S, wl.block_size), wl.block_size, 0.2,
+                                  wl.head_dim_v)
+        assert np.allclose(one[0][:, :, 0], ref[0], rtol=1e-13, atol=1e-14)
+        assert np.array_equal(np.isneginf(one[1][:, :, 0]), np.isneginf(ref[1]))
+
+
+def check_multi_brute():
+    """Pure-Python causal attention (exact sums) on a tiny MLA case, shards merged."""
+    rng = np.random.default_rng(22)
+    T, H, D, Dv, bs, L, S = 3, 2, 5, 3, 2, 7, 3
+    rows = rng.standard_normal((L, D))
+    table = np.array([[3, 0, 2, 1]], dtype=np.int32)
+    cache = np.zeros((4, bs, D))
+    for t in range(L):
+        cache[table[0, t // bs], t % bs] = rows[t]
+    q = rng.standard_normal((1, T, H, D))
+    _, _, _, o, lse = O.sharded_attention_multi("mla", "f32", q.astype(np.float32),
+                                                (cache.astype(np.float32),), table, [L], S, bs,
+                                                0.7, Dv)
+    r32 = cache.astype(np.float32).astype(np.float64)
+    q32 = q.astype(np.float32).astype(np.float64)
+    for j in range(T):
+        seen = [r32[table[0, t // bs], t % bs] for t in range(L - T + j + 1)]
+        for h in range(H):
+            bo, bl = _brute_attention(q32[0, j, h:h + 1], np.stack(seen),
+                                      np.stack(seen)[:, :Dv], 0.7)
+            assert np.allclose(o[0, j, h], bo[0], rtol=1e-12, atol=1e-13)
+            assert math.isclose(lse[0, j, h], bl[0], rel_tol=1e-13)
+
+
 # ------------------------------------------------------------------ KV append
 
 def check_append_example():
@@ -445,6 +526,9 @@ ALL_CHECKS = [
     check_gqa_head_groups,
     check_mla_value_is_latent_prefix,
     check_sharded_equals_full,
+    check_multi_hand_example,
+    check_multi_rows_are_prefix_decodes,
+    check_multi_brute,
     check_append_example,
     check_append_replay,
     check_append_owner_brute,

@@ -19,6 +19,7 @@ _gf = O._gather_fast
 _partial = O.partial_attention
 _up = O.bf16_bits_to_f64
 _append = O.append_token
+_multi = O.partial_attention_multi
 
 
 def m_attn_no_scale(q, k, v, scale):
@@ -191,6 +192,42 @@ def m_append_k_gets_v(kind, caches, new_rows, table, seq_lens, bs, S):
     return _append(kind, caches, (new_rows[1], new_rows[0]), table, seq_lens, bs, S)
 
 
+def _multi_with_positions(pos_of, kind, dtype, q, caches, table, bounds, bs, scale, dv,
+                          seqs=None):
+    """The oracle's causal partials with query token j placed at pos_of(L, T, j)."""
+    B, T, Hq = q.shape[:3]
+    S = bounds.shape[1]
+    po = np.zeros((B, S, T, Hq, dv))
+    pl = np.full((B, S, T, Hq), -np.inf)
+    for b in range(B):
+        L = int(np.max(bounds[b, :, 1]))
+        for j in range(T):
+            pos = pos_of(L, T, j)
+            nb = np.array(bounds[b:b + 1], copy=True)
+            nb[..., 1] = np.minimum(nb[..., 1], max(0, pos + 1))
+            nb[..., 0] = np.minimum(nb[..., 0], nb[..., 1])
+            o, l = _multi(kind, dtype, q[b:b + 1, j:j + 1], caches, table[b:b + 1], nb, bs, scale,
+                          dv)
+            po[b, :, j], pl[b, :, j] = o[0, :, 0], l[0, :, 0]
+    return po, pl
+
+
+def m_multi_excludes_own_token(*args, **kw):
+    return _multi_with_positions(lambda L, T, j: L - T + j - 1, *args, **kw)
+
+
+def m_multi_positions_from_zero(*args, **kw):
+    return _multi_with_positions(lambda L, T, j: j, *args, **kw)
+
+
+def m_multi_no_causal_mask(*args, **kw):
+    return _multi_with_positions(lambda L, T, j: L - 1, *args, **kw)
+
+
+def m_multi_tokens_reversed(*args, **kw):
+    return _multi_with_positions(lambda L, T, j: L - 1 - j, *args, **kw)
+
+
 MUTANTS = [
     ("attention", m_attn_no_scale),
     ("attention", m_attn_log2),
@@ -210,6 +247,10 @@ MUTANTS = [
     ("partial_attention", m_partial_interleaved_heads),
     ("partial_attention", m_partial_value_suffix),
     ("bf16_bits_to_f64", m_upcast_shift15),
+    ("partial_attention_multi", m_multi_excludes_own_token),
+    ("partial_attention_multi", m_multi_positions_from_zero),
+    ("partial_attention_multi", m_multi_no_causal_mask),
+    ("partial_attention_multi", m_multi_tokens_reversed),
     ("append_token", m_append_slot_page_swapped),
     ("append_token", m_append_next_position),
     ("append_token", m_append_owner_from_old_length),
