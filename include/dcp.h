@@ -180,6 +180,39 @@ dcp_status dcp_decode_attn(const dcp_attn_shape* shape, const void* q, const voi
                            void* stream);
 
 /*
+ * Several query tokens per request (speculative decoding / MTP verification). Both pages name
+ * speculative decoding and MTP as what DCP is to be combined with (Qiita article, section
+ * on how to view it in practice; naphjohn blog, section 5). A step then scores the q_len
+ * newest tokens of each request at once: query token j of request b sits at context position
+ * L_b - q_len + j, where L_b is the largest end among b's ranges in `bounds`, its K/V is
+ * already in the cache, and it sees the positions up to and including its own (causal
+ * order). The shards, the partials and the merge are as for one token; a row that sees
+ * nothing in a shard gets O_s = 0, LSE_s = -inf, and one that sees nothing at all (L_b <
+ * q_len - j) gets O = 0, LSE = -inf. q_len = 1 is exactly dcp_decode_attn[_partial].
+ *   q_len:     1 .. 16 query tokens per request.
+ *   q:         device [B][q_len][Hq][Dqk] (dtype).
+ *   part_o:    device float [B][S][q_len][Hq][Dv];  part_lse: device float [B][S][q_len][Hq].
+ *   out:       device float [B][q_len][Hq][Dv];     out_lse:  device float [B][q_len][Hq] or NULL.
+ *   The other arguments, the workspace rules and the errors are those of the one-token calls;
+ *   the workspace must hold dcp_workspace_bytes_multi(shape, q_len) bytes. dcp_merge_lse merges
+ *   these partials when called with num_heads = q_len * Hq.
+ * The KV pages are streamed once per group of query rows that share them: MLA takes up to 128
+ * rows (q_len * Hq) in one pass, GQA up to 16 rows (q_len * Hq / Hkv) per KV head. Errors
+ * additionally: DCP_ERR_SHAPE for q_len outside [1, 16].
+ */
+dcp_status dcp_workspace_bytes_multi(const dcp_attn_shape* shape, int32_t q_len, size_t* bytes);
+dcp_status dcp_decode_attn_multi_partial(const dcp_attn_shape* shape, int32_t q_len,
+                                         const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_table, const int32_t* bounds,
+                                         float* part_o, float* part_lse, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+dcp_status dcp_decode_attn_multi(const dcp_attn_shape* shape, int32_t q_len, const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* bounds,
+                                 void* workspace, size_t workspace_bytes, float* out,
+                                 float* out_lse, void* stream);
+
+/*
  * dcp_read_device_flags -- copy the sticky device-side flag word out of a workspace and
  * wait for `stream`. Bit 0: a bound was clamped into [0, max_blocks_per_seq*block_size] or
  * had end < start. Bit 1: a block id outside [0, num_blocks) was met and its tokens masked.

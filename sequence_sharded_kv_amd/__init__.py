@@ -26,6 +26,8 @@ from ._lib import (  # noqa: F401
     dcp_attn_shape,
     dcp_debug_gather_shard,
     dcp_decode_attn,
+    dcp_decode_attn_multi,
+    dcp_decode_attn_multi_partial,
     dcp_decode_attn_partial,
     dcp_kernel_timing_begin,
     dcp_kernel_timing_end,
@@ -36,13 +38,15 @@ from ._lib import (  # noqa: F401
     dcp_read_device_flags,
     dcp_status_string,
     dcp_workspace_bytes,
+    dcp_workspace_bytes_multi,
     load,
     make_shape,
 )
 
 
-def alloc_workspace(shape, device):
-    """One workspace for `shape` (reuse it across calls; see dcp_workspace_bytes)."""
+def alloc_workspace(shape, device, q_len: int = 1):
+    """One workspace for `shape` and `q_len` query tokens per request (reuse it across calls;
+    see dcp_workspace_bytes / dcp_workspace_bytes_multi)."""
     import torch
-    n = dcp_workspace_bytes(shape)
+    n = dcp_workspace_bytes_multi(shape, q_len)
     return torch.empty(n, dtype=torch.uint8, device=device)

@@ -35,6 +35,7 @@ EXPORTS = (
     "dcp_plan_shards_device", "dcp_workspace_bytes", "dcp_decode_attn_partial", "dcp_merge_lse",
     "dcp_decode_attn", "dcp_read_device_flags", "dcp_debug_gather_shard",
     "dcp_kernel_timing_begin", "dcp_kernel_timing_end", "dcp_append_kv",
+    "dcp_workspace_bytes_multi", "dcp_decode_attn_multi_partial", "dcp_decode_attn_multi",
 )
 
 
@@ -84,6 +85,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "dcp_kernel_timing_begin": (I32, [I32]),
         "dcp_kernel_timing_end": (I32, [ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_float)]),
         "dcp_append_kv": (I32, [SH, P, P, P, P, P, P, P, P]),
+        "dcp_workspace_bytes_multi": (I32, [SH, I32, ctypes.POINTER(SZ)]),
+        "dcp_decode_attn_multi_partial": (I32, [SH, I32, P, P, P, P, P, P, P, P, SZ, P]),
+        "dcp_decode_attn_multi": (I32, [SH, I32, P, P, P, P, P, P, SZ, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -178,6 +182,28 @@ def dcp_decode_attn(shape: dcp_attn_shape, q, k_cache, v_cache, block_table, bou
                     out, out_lse=None) -> None:
     _check(load().dcp_decode_attn(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(bounds), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+        _ptr(out_lse), _stream(q)))
+
+
+def dcp_workspace_bytes_multi(shape: dcp_attn_shape, q_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().dcp_workspace_bytes_multi(ctypes.byref(shape), q_len, ctypes.byref(n)))
+    return int(n.value)
+
+
+def dcp_decode_attn_multi_partial(shape: dcp_attn_shape, q_len: int, q, k_cache, v_cache,
+                                  block_table, bounds, part_o, part_lse, workspace) -> None:
+    _check(load().dcp_decode_attn_multi_partial(
+        ctypes.byref(shape), q_len, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(bounds), _ptr(part_o), _ptr(part_lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q)))
+
+
+def dcp_decode_attn_multi(shape: dcp_attn_shape, q_len: int, q, k_cache, v_cache, block_table,
+                          bounds, workspace, out, out_lse=None) -> None:
+    _check(load().dcp_decode_attn_multi(
+        ctypes.byref(shape), q_len, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(bounds), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
         _ptr(out_lse), _stream(q)))
 

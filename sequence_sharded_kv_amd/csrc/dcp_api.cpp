@@ -93,31 +93,44 @@ dcp_status check_shape(const dcp_attn_shape* sh) {
   return DCP_OK;
 }
 
-dcp_status make_plan(const dcp_attn_shape* sh, dcp::Plan* plan) {
+// Most query tokens per request that the multi-token entry points take.
+constexpr int32_t kMaxQueryTokens = 16;
+
+dcp_status make_plan(const dcp_attn_shape* sh, int32_t Tq, dcp::Plan* plan) {
   dcp_status st = check_shape(sh);
   if (st != DCP_OK) return st;
+  if (Tq < 1 || Tq > kMaxQueryTokens)
+    return fail(DCP_ERR_SHAPE, "q_len %d outside [1, %d]", Tq, kMaxQueryTokens);
   using dcp::Kernel;
   Kernel k = Kernel::kNone;
-  int32_t units, hu, pmax;
+  int32_t ru, pmax;
+  const int32_t G = sh->num_q_heads / sh->num_kv_heads;
+  const int32_t rows = G * Tq;  // rows that read one KV head
   if (sh->kv_kind == DCP_KV_GQA) {
-    const int32_t G = sh->num_q_heads / sh->num_kv_heads;
     const int32_t D = sh->head_dim_qk;
     if (sh->dtype == DCP_BF16 && G <= 16 && (D == 64 || D == 128))
       k = Kernel::kGqaMfma;
     else if (G <= 16 && D % 64 == 0 && D <= 256)
       k = Kernel::kGqaValu;
-    units = sh->batch * sh->num_shards * sh->num_kv_heads;
-    hu = G;
+    ru = rows < 16 ? rows : 16;  // one 16-column MFMA block (or 16 VALU rows) per unit
     pmax = kMaxWorkersWave;
   } else {
     if (sh->dtype == DCP_BF16 && sh->head_dim_qk == 576 && sh->head_dim_v == 512 &&
         (sh->num_q_heads == 16 || sh->num_q_heads == 32 || sh->num_q_heads == 64 ||
          sh->num_q_heads == 128))
       k = Kernel::kMlaMfma;
-    units = sh->batch * sh->num_shards;
-    hu = sh->num_q_heads;
+    // waves of 16 rows, a power of two of them up to 8 per workgroup
+    ru = 16;
+    while (ru < rows && ru < 128) ru *= 2;
     pmax = kMaxWorkersMla;
   }
+  const int32_t groups = (rows + ru - 1) / ru;
+  const int64_t units64 = (int64_t)sh->batch * sh->num_shards *
+                          (sh->kv_kind == DCP_KV_GQA ? sh->num_kv_heads : 1) * groups;
+  if (units64 * (int64_t)sh->max_blocks_per_seq > INT32_MAX)
+    return fail(DCP_ERR_SHAPE, "units (%lld) * max_blocks_per_seq exceeds int32",
+                (long long)units64);
+  const int32_t units = (int32_t)units64;
   if (k == Kernel::kNone)
     return fail(DCP_ERR_UNSUPPORTED,
                 "no kernel for kv_kind=%d dtype=%d Hq=%d Hkv=%d Dqk=%d Dv=%d (GQA: group <= 16, "
@@ -127,19 +140,22 @@ dcp_status make_plan(const dcp_attn_shape* sh, dcp::Plan* plan) {
                 sh->head_dim_v);
   plan->kernel = k;
   plan->units = units;
-  plan->heads_per_unit = hu;
+  plan->rows_per_unit = ru;
+  plan->row_groups = groups;
   plan->max_workers = pmax;
   dcp::WsLayout& w = plan->ws;
-  const size_t B = sh->batch, S = sh->num_shards, Hq = sh->num_q_heads, Dv = sh->head_dim_v;
+  const size_t B = sh->batch, S = sh->num_shards, R = (size_t)sh->num_q_heads * Tq;
+  const size_t Dv = sh->head_dim_v;
   size_t off = 0;
   w.flags = off;       off = align_up(off + dcp::kWsHeadBytes);
   w.pre = off;         off = align_up(off + sizeof(int32_t) * ((size_t)units + 1));
   w.fin = off;         off = align_up(off + sizeof(int32_t) * 4 * (size_t)units);
   w.ubounds = off;     off = align_up(off + sizeof(int32_t) * B * S * 2);
-  w.piece_o = off;     off = align_up(off + sizeof(float) * 2 * (size_t)pmax * hu * Dv);
-  w.piece_lse = off;   off = align_up(off + sizeof(float) * 2 * (size_t)pmax * hu);
-  w.part_o = off;      off = align_up(off + sizeof(float) * B * S * Hq * Dv);
-  w.part_lse = off;    off = align_up(off + sizeof(float) * B * S * Hq);
+  w.qend = off;        off = align_up(off + sizeof(int32_t) * B);
+  w.piece_o = off;     off = align_up(off + sizeof(float) * 2 * (size_t)pmax * ru * Dv);
+  w.piece_lse = off;   off = align_up(off + sizeof(float) * 2 * (size_t)pmax * ru);
+  w.part_o = off;      off = align_up(off + sizeof(float) * B * S * R * Dv);
+  w.part_lse = off;    off = align_up(off + sizeof(float) * B * S * R);
   w.total = off;
   return DCP_OK;
 }
@@ -151,12 +167,12 @@ dcp_status device_fail(hipError_t e, const char* what) {
 }
 
 // Shared front half of the two attention entry points.
-dcp_status run_partials(const dcp_attn_shape* sh, const void* q, const void* k, const void* v,
-                        const int32_t* block_table, const int32_t* bounds, float* part_o,
-                        float* part_lse, void* workspace, size_t workspace_bytes, void* stream,
-                        dcp::Plan* plan_out, dcp::AttnArgs* args_out, bool fused) {
+dcp_status run_partials(const dcp_attn_shape* sh, int32_t Tq, const void* q, const void* k,
+                        const void* v, const int32_t* block_table, const int32_t* bounds,
+                        float* part_o, float* part_lse, void* workspace, size_t workspace_bytes,
+                        void* stream, dcp::Plan* plan_out, dcp::AttnArgs* args_out, bool fused) {
   dcp::Plan plan;
-  dcp_status st = make_plan(sh, &plan);
+  dcp_status st = make_plan(sh, Tq, &plan);
   if (st != DCP_OK) return st;
   if (!q || !k || !block_table || !bounds || !workspace || (!fused && (!part_o || !part_lse)))
     return fail(DCP_ERR_NULL, "q, k_cache, block_table, bounds, workspace%s must be non-NULL",
@@ -183,6 +199,7 @@ dcp_status run_partials(const dcp_attn_shape* sh, const void* q, const void* k, 
   a.ubounds = reinterpret_cast<int32_t*>(ws + plan.ws.ubounds);
   a.pre = reinterpret_cast<int32_t*>(ws + plan.ws.pre);
   a.fin = reinterpret_cast<int32_t*>(ws + plan.ws.fin);
+  a.qend = reinterpret_cast<int32_t*>(ws + plan.ws.qend);
   a.part_o = fused ? reinterpret_cast<float*>(ws + plan.ws.part_o) : part_o;
   a.part_lse = fused ? reinterpret_cast<float*>(ws + plan.ws.part_lse) : part_lse;
   a.piece_o = reinterpret_cast<float*>(ws + plan.ws.piece_o);
@@ -200,18 +217,23 @@ dcp_status run_partials(const dcp_attn_shape* sh, const void* q, const void* k, 
   a.max_blocks = sh->max_blocks_per_seq;
   a.num_blocks = sh->num_blocks;
   a.U = plan.units;
+  a.Tq = Tq;
+  a.R = sh->num_q_heads * Tq;
+  a.Ru = plan.rows_per_unit;
+  a.NRg = plan.row_groups;
   a.scale_log2 = sh->softmax_scale * 1.4426950408889634f;
   switch (plan.kernel) {
     case dcp::Kernel::kGqaMfma: a.P = dcp::gqa_mfma_workers(dev, a.Dqk, plan.max_workers); break;
     case dcp::Kernel::kGqaValu: a.P = dcp::gqa_valu_workers(dev, plan.max_workers); break;
-    case dcp::Kernel::kMlaMfma: a.P = dcp::mla_mfma_workers(dev, a.Hq, plan.max_workers); break;
+    case dcp::Kernel::kMlaMfma: a.P = dcp::mla_mfma_workers(dev, a.Ru, plan.max_workers); break;
     default: return fail(DCP_ERR_UNSUPPORTED, "no kernel");
   }
   hipStream_t s = as_stream(stream);
   const int32_t units_per_bs = plan.units / (sh->batch * sh->num_shards);
   e = dcp::launch_schedule(bounds, a.B, a.S, units_per_bs, a.P,
                            reinterpret_cast<int32_t*>(ws + plan.ws.fin), a.bs, a.max_blocks,
-                           const_cast<int32_t*>(a.ubounds), const_cast<int32_t*>(a.pre), a.flags, s);
+                           const_cast<int32_t*>(a.ubounds), const_cast<int32_t*>(a.pre), a.flags,
+                           Tq, const_cast<int32_t*>(a.qend), s);
   if (e != hipSuccess) return device_fail(e, "schedule launch");
   const bool timed = g_timing.on && g_timing.used < g_timing.start.size();
   if (timed) {
@@ -229,7 +251,7 @@ dcp_status run_partials(const dcp_attn_shape* sh, const void* q, const void* k, 
     e = hipEventRecord(g_timing.stop[g_timing.used++], s);
     if (e != hipSuccess) return device_fail(e, "timing event");
   }
-  e = dcp::launch_finish_units(a, plan.heads_per_unit, s);
+  e = dcp::launch_finish_units(a, s);
   if (e != hipSuccess) return device_fail(e, "finish launch");
   *plan_out = plan;
   *args_out = a;
@@ -291,13 +313,29 @@ dcp_status dcp_plan_shards_device(const int32_t* seq_lens, int32_t batch, int32_
   return ok();
 }
 
-dcp_status dcp_workspace_bytes(const dcp_attn_shape* shape, size_t* bytes) {
+dcp_status dcp_workspace_bytes_multi(const dcp_attn_shape* shape, int32_t q_len, size_t* bytes) {
   if (!bytes) return fail(DCP_ERR_NULL, "bytes is NULL");
   dcp::Plan plan;
-  dcp_status st = make_plan(shape, &plan);
+  dcp_status st = make_plan(shape, q_len, &plan);
   if (st != DCP_OK) return st;
   *bytes = plan.ws.total;
   return ok();
+}
+
+dcp_status dcp_workspace_bytes(const dcp_attn_shape* shape, size_t* bytes) {
+  return dcp_workspace_bytes_multi(shape, 1, bytes);
+}
+
+dcp_status dcp_decode_attn_multi_partial(const dcp_attn_shape* shape, int32_t q_len,
+                                         const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_table, const int32_t* bounds,
+                                         float* part_o, float* part_lse, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  dcp::Plan plan;
+  dcp::AttnArgs a;
+  dcp_status st = run_partials(shape, q_len, q, k_cache, v_cache, block_table, bounds, part_o,
+                               part_lse, workspace, workspace_bytes, stream, &plan, &a, false);
+  return st == DCP_OK ? ok() : st;
 }
 
 dcp_status dcp_decode_attn_partial(const dcp_attn_shape* shape, const void* q,
@@ -305,11 +343,8 @@ dcp_status dcp_decode_attn_partial(const dcp_attn_shape* shape, const void* q,
                                    const int32_t* block_table, const int32_t* bounds,
                                    float* part_o, float* part_lse, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-  dcp::Plan plan;
-  dcp::AttnArgs a;
-  dcp_status st = run_partials(shape, q, k_cache, v_cache, block_table, bounds, part_o, part_lse,
-                               workspace, workspace_bytes, stream, &plan, &a, false);
-  return st == DCP_OK ? ok() : st;
+  return dcp_decode_attn_multi_partial(shape, 1, q, k_cache, v_cache, block_table, bounds,
+                                       part_o, part_lse, workspace, workspace_bytes, stream);
 }
 
 dcp_status dcp_merge_lse(int32_t batch, int32_t num_shards, int32_t num_heads, int32_t head_dim_v,
@@ -328,21 +363,30 @@ dcp_status dcp_merge_lse(int32_t batch, int32_t num_shards, int32_t num_heads, i
   return ok();
 }
 
-dcp_status dcp_decode_attn(const dcp_attn_shape* shape, const void* q, const void* k_cache,
-                           const void* v_cache, const int32_t* block_table, const int32_t* bounds,
-                           void* workspace, size_t workspace_bytes, float* out, float* out_lse,
-                           void* stream) {
+dcp_status dcp_decode_attn_multi(const dcp_attn_shape* shape, int32_t q_len, const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* bounds,
+                                 void* workspace, size_t workspace_bytes, float* out,
+                                 float* out_lse, void* stream) {
   if (!out) return fail(DCP_ERR_NULL, "out must be non-NULL");
   if (!aligned16(out)) return fail(DCP_ERR_ALIGN, "out must be 16-byte aligned");
   dcp::Plan plan;
   dcp::AttnArgs a;
-  dcp_status st = run_partials(shape, q, k_cache, v_cache, block_table, bounds, nullptr, nullptr,
-                               workspace, workspace_bytes, stream, &plan, &a, true);
+  dcp_status st = run_partials(shape, q_len, q, k_cache, v_cache, block_table, bounds, nullptr,
+                               nullptr, workspace, workspace_bytes, stream, &plan, &a, true);
   if (st != DCP_OK) return st;
-  hipError_t e = dcp::launch_merge(a.B, a.S, a.Hq, a.Dv, a.part_o, a.part_lse, out, out_lse,
+  hipError_t e = dcp::launch_merge(a.B, a.S, a.R, a.Dv, a.part_o, a.part_lse, out, out_lse,
                                    as_stream(stream));
   if (e != hipSuccess) return device_fail(e, "merge launch");
   return ok();
+}
+
+dcp_status dcp_decode_attn(const dcp_attn_shape* shape, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table, const int32_t* bounds,
+                           void* workspace, size_t workspace_bytes, float* out, float* out_lse,
+                           void* stream) {
+  return dcp_decode_attn_multi(shape, 1, q, k_cache, v_cache, block_table, bounds, workspace,
+                               workspace_bytes, out, out_lse, stream);
 }
 
 dcp_status dcp_read_device_flags(const void* workspace, int32_t* flags, void* stream) {

@@ -20,9 +20,17 @@ constexpr int32_t kFlagBadBlock = 2;
 
 // Work is split stream-K style: every (unit, page) pair is one page of work, the pages of
 // all units are concatenated in unit order, and worker w takes the contiguous range
-// [w*T/P, (w+1)*T/P). A unit is (request, shard) for MLA and (request, shard, kv head) for
-// GQA. A unit cut by a worker boundary yields pieces (partials over sub-ranges) that a
-// finishing pass merges into the unit's partial.
+// [w*T/P, (w+1)*T/P). A unit is (request, shard, row group) for MLA and (request, shard,
+// kv head, row group) for GQA. A unit cut by a worker boundary yields pieces (partials over
+// sub-ranges) that a finishing pass merges into the unit's partial.
+//
+// Query rows: a request scores Tq query tokens (1 for plain decode) against its context;
+// row rho = j * Hq + h is head h of query token j (R = Tq * Hq rows per request). The rows
+// that read one KV head (its G heads of every token: G * Tq rows; MLA: G = Hq) are cut into
+// groups of Ru rows, one unit each. Local row r of group rg is rr = rg * Ru + r of that
+// space (rows with rr >= G * Tq are padding), i.e. token j = rr / G, head kvh * G + rr % G.
+// Token j sits at position qend[b] + j, qend[b] = L_b - Tq with L_b the largest end among
+// the request's ranges, and sees the context positions up to its own.
 //
 // Workspace layout (offsets 256-byte aligned):
 //   flags      int32[64]  sticky device flag word at [0], the number of entries of `fin` at
@@ -33,20 +41,22 @@ constexpr int32_t kFlagBadBlock = 2;
 //                                worker, 0) for units cut by worker boundaries, (u, -1, -1, 0)
 //                                for units with no pages; unordered
 //   ubounds    int32[B*S*2]      sanitised (start, end) per (request, shard)
-//   piece_o    float[2*Pmax][Hu][Dv]
-//   piece_lse  float[2*Pmax][Hu]
-//   part_o     float[B][S][Hq][Dv]   (fused path only)
-//   part_lse   float[B][S][Hq]
+//   qend       int32[B]          position of each request's first query token
+//   piece_o    float[2*Pmax][Ru][Dv]
+//   piece_lse  float[2*Pmax][Ru]
+//   part_o     float[B][S][R][Dv]    (fused path only)
+//   part_lse   float[B][S][R]
 struct WsLayout {
-  size_t flags, pre, fin, ubounds, piece_o, piece_lse, part_o, part_lse, total;
+  size_t flags, pre, fin, ubounds, qend, piece_o, piece_lse, part_o, part_lse, total;
 };
 
 enum class Kernel { kNone = 0, kGqaValu, kGqaMfma, kMlaMfma };
 
 struct Plan {          // host-side decisions for one shape
   Kernel kernel;
-  int32_t units;       // U
-  int32_t heads_per_unit;  // Hu
+  int32_t units;           // U
+  int32_t rows_per_unit;   // Ru
+  int32_t row_groups;      // row groups per KV head
   int32_t max_workers;     // Pmax
   WsLayout ws;
 };
@@ -60,15 +70,27 @@ struct AttnArgs {
   const int32_t* ubounds;   // [B*S][2]
   const int32_t* pre;       // [U + 1]
   const int32_t* fin;       // [U][4], count in flags[1]
-  float* part_o;            // [B][S][Hq][Dv]
-  float* part_lse;          // [B][S][Hq]
-  float* piece_o;           // [2P][Hu][Dv]
-  float* piece_lse;         // [2P][Hu]
+  const int32_t* qend;      // [B]
+  float* part_o;            // [B][S][R][Dv]
+  float* part_lse;          // [B][S][R]
+  float* piece_o;           // [2P][Ru][Dv]
+  float* piece_lse;         // [2P][Ru]
   int32_t* flags;
   const char* zero_row;     // kWsZeroWords*4 bytes of zeros in the workspace
   int32_t B, S, Hq, Hkv, G, Dqk, Dv, bs, max_blocks, num_blocks, U, P;
+  int32_t Tq, R, Ru, NRg;   // query tokens, rows per request, rows per unit, groups per KV head
   float scale_log2;         // softmax_scale * log2(e)
 };
+
+// Query row of local row `r` of row group `rg` of KV head `kvh` (see "Query rows" above):
+// returns rho, or -1 for a padding row; *j receives the query token.
+__host__ __device__ inline int32_t unit_row(const AttnArgs& a, int32_t kvh, int32_t rg, int32_t r,
+                                            int32_t* j) {
+  const int32_t rr = rg * a.Ru + r;
+  if (r >= a.Ru || rr >= a.G * a.Tq) return -1;
+  *j = rr / a.G;
+  return *j * a.Hq + kvh * a.G + (rr - *j * a.G);
+}
 
 // Launchers (each returns the hipError_t of its launch).
 hipError_t launch_plan_device(const int32_t* seq_lens, int32_t B, int32_t S, int32_t bs,
@@ -76,8 +98,8 @@ hipError_t launch_plan_device(const int32_t* seq_lens, int32_t B, int32_t S, int
 hipError_t launch_schedule(const int32_t* bounds, int32_t B, int32_t S, int32_t units_per_bs,
                            int32_t P, int32_t* fin,
                            int32_t bs, int32_t max_blocks, int32_t* ubounds, int32_t* pre,
-                           int32_t* flags, hipStream_t stream);
-hipError_t launch_finish_units(const AttnArgs& a, int32_t Hu, hipStream_t stream);
+                           int32_t* flags, int32_t Tq, int32_t* qend, hipStream_t stream);
+hipError_t launch_finish_units(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_merge(int32_t B, int32_t S, int32_t H, int32_t Dv, const float* part_o,
                         const float* part_lse, float* out, float* out_lse, hipStream_t stream);
 hipError_t launch_debug_gather(const dcp_attn_shape& sh, const void* cache,
@@ -93,7 +115,7 @@ int32_t gqa_valu_workers(int device, int32_t max_workers);
 hipError_t launch_gqa_valu(const AttnArgs& a, int32_t dtype, hipStream_t stream);
 int32_t gqa_mfma_workers(int device, int32_t Dqk, int32_t max_workers);
 hipError_t launch_gqa_mfma(const AttnArgs& a, hipStream_t stream);
-int32_t mla_mfma_workers(int device, int32_t Hq, int32_t max_workers);
+int32_t mla_mfma_workers(int device, int32_t Ru, int32_t max_workers);
 hipError_t launch_mla_mfma(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace dcp

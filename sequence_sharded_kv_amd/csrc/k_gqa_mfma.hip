@@ -82,7 +82,6 @@ gqa_mfma_kernel(AttnArgs a) {
   const int64_t T_pages = a.pre[a.U];
   const int64_t g0 = worker_begin(T_pages, a.P, w), g1 = worker_begin(T_pages, a.P, w + 1);
   if (g0 >= g1) return;
-  const int G = a.G;
   const int32_t bs = a.bs;
   const bool bs_pow2 = (bs & (bs - 1)) == 0;
   const int bs_shift = __builtin_ctz((unsigned)bs);
@@ -94,7 +93,9 @@ gqa_mfma_kernel(AttnArgs a) {
     while ((int64_t)a.pre[u + 1] <= g) ++u;
     const int64_t up0 = a.pre[u], up1 = a.pre[u + 1];
     const int64_t sg1 = up1 < g1 ? up1 : g1;
-    const int32_t bsi = u / a.Hkv, kvh = u % a.Hkv;
+    const int32_t per_bs = a.Hkv * a.NRg;
+    const int32_t bsi = u / per_bs, hsub = u - bsi * per_bs;
+    const int32_t kvh = hsub / a.NRg, rg = hsub - kvh * a.NRg;
     const int32_t b = bsi / a.S;
     const int64_t ta = a.ubounds[2 * bsi], te = a.ubounds[2 * bsi + 1];
     const int64_t pa = ta / bs;
@@ -107,11 +108,16 @@ gqa_mfma_kernel(AttnArgs a) {
     // Token positions fit in 32 bits (max_blocks_per_seq * block_size <= INT32_MAX).
     const int32_t t0i = (int32_t)t0, t1i = (int32_t)t1;
 
-    // Q^T as the B operand: lane (n, gq) holds q[n][32j + 8gq .. +8]
+    // MFMA column n is query row rho (head of KV head kvh, query token jq), or padding; lim is
+    // the last context position the row may see.
+    int32_t jq = 0;
+    const int32_t rho = unit_row(a, kvh, rg, n, &jq);
+    const bool hv = rho >= 0;
+    const int32_t lim = a.Tq == 1 ? INT32_MAX : a.qend[b] + jq;
+    // Q^T as the B operand: lane (n, gq) holds q[rho][32j + 8gq .. +8]
     bf16x8 qop[C::kSteps];
     {
-      const bool hv = n < G;
-      const uint16_t* qrow = Q + ((int64_t)b * a.Hq + kvh * G + (hv ? n : 0)) * D;
+      const uint16_t* qrow = Q + ((int64_t)b * a.R + (hv ? rho : 0)) * D;
 #pragma unroll
       for (int j = 0; j < C::kSteps; ++j) {
         u32x4 raw = *(const u32x4*)(qrow + 32 * j + 8 * gq);
@@ -191,8 +197,10 @@ gqa_mfma_kernel(AttnArgs a) {
           s[at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[at][j]),
                                                           qop[j], s[at], 0, 0, 0);
       }
-      // online softmax: lane holds tokens 16at + 4gq + i of head n
-      const uint32_t mask = cur.mask;
+      // online softmax: lane holds tokens 16at + 4gq + i of row n (its valid tokens up to lim)
+      const int32_t dl = lim - tile;
+      const uint32_t mask =
+          cur.mask & (dl < 0 ? 0u : dl >= kGqaTile - 1 ? 0xFFFFFFFFu : (2u << dl) - 1u);
       float x[8];
       float tmax = kNegInf;
 #pragma unroll
@@ -252,18 +260,17 @@ gqa_mfma_kernel(AttnArgs a) {
     float* dst_o;
     float* dst_l;
     if (whole) {
-      dst_o = a.part_o + ((int64_t)bsi * a.Hq + kvh * G) * D;
-      dst_l = a.part_lse + (int64_t)bsi * a.Hq + kvh * G;
+      dst_o = a.part_o + ((int64_t)bsi * a.R + rho) * D;
+      dst_l = a.part_lse + (int64_t)bsi * a.R + rho;
     } else {
       int32_t slot = piece_slot(w, first);
-      dst_o = a.piece_o + (int64_t)slot * G * D;
-      dst_l = a.piece_lse + (int64_t)slot * G;
+      dst_o = a.piece_o + ((int64_t)slot * a.Ru + n) * D;
+      dst_l = a.piece_lse + (int64_t)slot * a.Ru + n;
     }
-    if (n < G) {
+    if (hv) {
 #pragma unroll
-      for (int mt = 0; mt < C::kMt; ++mt)
-        *(f32x4*)(dst_o + (int64_t)n * D + 16 * mt + 4 * gq) = acc[mt] * inv;
-      if (gq == 0) dst_l[n] = l > 0.f ? (m_run + fast_log2(l)) * kLn2 : kNegInf;
+      for (int mt = 0; mt < C::kMt; ++mt) *(f32x4*)(dst_o + 16 * mt + 4 * gq) = acc[mt] * inv;
+      if (gq == 0) *dst_l = l > 0.f ? (m_run + fast_log2(l)) * kLn2 : kNegInf;
     }
     g = sg1;
   }

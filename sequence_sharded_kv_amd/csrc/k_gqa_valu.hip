@@ -43,7 +43,6 @@ gqa_valu_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int D = NDV * 64;
-  const int G = a.G;
   float* qs = valu_lds + wv * (kValuMaxG * D + kValuMaxG * 64);  // [G][D]
   float* ps = qs + kValuMaxG * D;                                 // [G][64]
   const int32_t w = blockIdx.x * kValuWaves + wv;
@@ -61,8 +60,11 @@ gqa_valu_kernel(AttnArgs a) {
     while ((int64_t)a.pre[u + 1] <= g) ++u;
     const int64_t up0 = a.pre[u], up1 = a.pre[u + 1];
     const int64_t sg1 = up1 < g1 ? up1 : g1;
-    const int32_t bsi = u / a.Hkv, kvh = u % a.Hkv;
+    const int32_t per_bs = a.Hkv * a.NRg;
+    const int32_t bsi = u / per_bs, hsub = u - bsi * per_bs;
+    const int32_t kvh = hsub / a.NRg, rg = hsub - kvh * a.NRg;
     const int32_t b = bsi / a.S;
+    const int32_t Ru = a.Ru;
     const int64_t ta = a.ubounds[2 * bsi], te = a.ubounds[2 * bsi + 1];
     const int64_t pa = ta / a.bs;
     int64_t t0 = (pa + (g - up0)) * a.bs, t1 = (pa + (sg1 - up0)) * a.bs;
@@ -70,10 +72,20 @@ gqa_valu_kernel(AttnArgs a) {
     if (t1 > te) t1 = te;
     const bool whole = (g == up0) && (sg1 == up1);
     const bool first = (g == g0);
-    // q rows of this KV head's group -> LDS
-    for (int i = lane; i < G * D; i += 64) {
+    // the unit's query rows -> LDS (padding rows read as zeros)
+    for (int i = lane; i < Ru * D; i += 64) {
       int h = i / D, d = i % D;
-      qs[i] = Elem<T>::get(Q, ((int64_t)b * a.Hq + kvh * G + h) * a.Dqk + d);
+      int32_t jh = 0;
+      const int32_t rho = unit_row(a, kvh, rg, h, &jh);
+      qs[i] = rho >= 0 ? Elem<T>::get(Q, ((int64_t)b * a.R + rho) * a.Dqk + d) : 0.f;
+    }
+    // last context position each row may see (several query tokens)
+    int32_t lim[kValuMaxG];
+#pragma unroll
+    for (int h = 0; h < kValuMaxG; ++h) {
+      int32_t jh = 0;
+      const bool ok = unit_row(a, kvh, rg, h, &jh) >= 0;
+      lim[h] = (a.Tq == 1 || !ok) ? INT32_MAX : a.qend[b] + jh;
     }
     __builtin_amdgcn_wave_barrier();
     float m[kValuMaxG], lsum[kValuMaxG], acc[kValuMaxG][NDV];
@@ -104,7 +116,7 @@ gqa_valu_kernel(AttnArgs a) {
           for (int j = 0; j < 8; ++j) kv[j] = Elem<T>::get(K, row + d + j);
 #pragma unroll
           for (int h = 0; h < kValuMaxG; ++h) {
-            if (h < G) {
+            if (h < Ru) {
 #pragma unroll
               for (int j = 0; j < 8; ++j) s[h] = fmaf(qs[h * D + d + j], kv[j], s[h]);
             }
@@ -114,8 +126,8 @@ gqa_valu_kernel(AttnArgs a) {
       const int nvalid = (int)((t1 - tile) < 64 ? (t1 - tile) : 64);
 #pragma unroll
       for (int h = 0; h < kValuMaxG; ++h) {
-        if (h < G) {
-          float x = valid ? s[h] * a.scale_log2 : kNegInf;
+        if (h < Ru) {
+          float x = (valid && t <= lim[h]) ? s[h] * a.scale_log2 : kNegInf;
           float mn = fmaxf(m[h], wave_max(x));
           float alpha = (mn == kNegInf) ? 1.f : fast_exp2(m[h] - mn);
           float p = (x == kNegInf) ? 0.f : fast_exp2(x - mn);
@@ -137,7 +149,7 @@ gqa_valu_kernel(AttnArgs a) {
         for (int j = 0; j < NDV; ++j) vv[j] = Elem<T>::get(V, vrow + lane + 64 * j);
 #pragma unroll
         for (int h = 0; h < kValuMaxG; ++h) {
-          if (h < G) {
+          if (h < Ru) {
             float p = ps[h * 64 + tt];
 #pragma unroll
             for (int j = 0; j < NDV; ++j) acc[h][j] = fmaf(p, vv[j], acc[h][j]);
@@ -147,25 +159,21 @@ gqa_valu_kernel(AttnArgs a) {
       __builtin_amdgcn_wave_barrier();
     }
     // finalise and write this segment's partial
-    float* dst_o;
-    float* dst_l;
-    int64_t hstride = a.Dv;
-    if (whole) {
-      dst_o = a.part_o + ((int64_t)bsi * a.Hq + kvh * G) * a.Dv;
-      dst_l = a.part_lse + (int64_t)bsi * a.Hq + kvh * G;
-    } else {
-      int32_t slot = piece_slot(w, first);
-      dst_o = a.piece_o + (int64_t)slot * G * a.Dv;
-      dst_l = a.piece_lse + (int64_t)slot * G;
-    }
+    const int32_t slot = piece_slot(w, first);
 #pragma unroll
     for (int h = 0; h < kValuMaxG; ++h) {
-      if (h < G) {
+      int32_t jh = 0;
+      const int32_t rho = unit_row(a, kvh, rg, h, &jh);
+      if (rho >= 0) {
+        float* dst_o = whole ? a.part_o + ((int64_t)bsi * a.R + rho) * a.Dv
+                             : a.piece_o + ((int64_t)slot * Ru + h) * a.Dv;
+        float* dst_l = whole ? a.part_lse + (int64_t)bsi * a.R + rho
+                             : a.piece_lse + (int64_t)slot * Ru + h;
         float l = wave_sum(lsum[h]);
         float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-        for (int j = 0; j < NDV; ++j) dst_o[h * hstride + lane + 64 * j] = acc[h][j] * inv;
-        if (lane == 0) dst_l[h] = l > 0.f ? (m[h] + fast_log2(l)) * kLn2 : kNegInf;
+        for (int j = 0; j < NDV; ++j) dst_o[lane + 64 * j] = acc[h][j] * inv;
+        if (lane == 0) *dst_l = l > 0.f ? (m[h] + fast_log2(l)) * kLn2 : kNegInf;
       }
     }
     __builtin_amdgcn_wave_barrier();

@@ -125,7 +125,7 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
     while ((int64_t)a.pre[u + 1] <= g) ++u;
     const int64_t up0 = a.pre[u], up1 = a.pre[u + 1];
     const int64_t sg1 = up1 < g1 ? up1 : g1;
-    const int32_t bsi = u;               // one unit per (request, shard)
+    const int32_t bsi = u / a.NRg, rg = u - bsi * a.NRg;  // (request, shard), row group
     const int32_t b = bsi / a.S;
     const int64_t ta = a.ubounds[2 * bsi], te = a.ubounds[2 * bsi + 1];
     const int64_t pa = ta / a.bs;
@@ -202,10 +202,17 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
       return mask;
     };
 
-    // the wave's Q slice as the B operand: lane holds q[16wv + n][32j + 8gq .. +8]
+    // This wave's 16 query rows (head h of query token jq; 16 | Hq, so one token per wave)
+    // and the last context position they may see; rows past R are padding and not stored.
+    int32_t jq = 0;
+    const int32_t rho = unit_row(a, 0, rg, 16 * wv + n, &jq);
+    const bool row_ok = rho >= 0;
+    const int32_t lim = a.Tq == 1 ? INT32_MAX
+                                  : __builtin_amdgcn_readfirstlane(a.qend[b] + jq);
+    // the wave's Q slice as the B operand: lane holds q[row][32j + 8gq .. +8]
     bf16x8 qop[kMlaDqk / 32];
     {
-      const uint16_t* qrow = Q + ((int64_t)b * a.Hq + 16 * wv + n) * kMlaDqk + 8 * gq;
+      const uint16_t* qrow = Q + ((int64_t)b * a.R + (row_ok ? rho : 0)) * kMlaDqk + 8 * gq;
 #pragma unroll
       for (int j = 0; j < kMlaDqk / 32; ++j)
         qop[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 32 * j));
@@ -221,7 +228,10 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
     __syncthreads();
     int cur = 0;
     for (int32_t tile = t0i; tile < t1i; tile += kMlaTile) {
-      const uint32_t mask = mask_next;
+      // valid tokens, less those past the rows' own position (several query tokens)
+      const int32_t dl = lim - tile;
+      const uint32_t mask =
+          mask_next & (dl < 0 ? 0u : dl >= kMlaTile - 1 ? 0xFFFFFFFFu : (2u << dl) - 1u);
       constexpr int kQ = kRows / 2;  // rows queued before the scores
       const bool more = tile + kMlaTile < t1i;
       if (more) mask_next = issue_tile(tile + kMlaTile, cur ^ 1, false);
@@ -295,20 +305,22 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row) {
     // finalise this segment: l over the four lanes of head n
     const float l = quad_sum(l_run);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int head = 16 * wv + n;
     float* dst_o;
     float* dst_l;
     if (whole) {
-      dst_o = a.part_o + ((int64_t)bsi * a.Hq + head) * kMlaDv;
-      dst_l = a.part_lse + (int64_t)bsi * a.Hq + head;
+      dst_o = a.part_o + ((int64_t)bsi * a.R + rho) * kMlaDv;
+      dst_l = a.part_lse + (int64_t)bsi * a.R + rho;
     } else {
       const int32_t slot = piece_slot(w, first);
-      dst_o = a.piece_o + ((int64_t)slot * a.Hq + head) * kMlaDv;
-      dst_l = a.piece_lse + (int64_t)slot * a.Hq + head;
+      dst_o = a.piece_o + ((int64_t)slot * a.Ru + 16 * wv + n) * kMlaDv;
+      dst_l = a.piece_lse + (int64_t)slot * a.Ru + 16 * wv + n;
     }
+    if (row_ok) {
 #pragma unroll
-    for (int mt = 0; mt < kMlaDv / 16; ++mt) *(f32x4*)(dst_o + 16 * mt + 4 * gq) = acc[mt] * inv;
-    if (gq == 0) *dst_l = l > 0.f ? (m_run + fast_log2(l)) * kLn2 : kNegInf;
+      for (int mt = 0; mt < kMlaDv / 16; ++mt)
+        *(f32x4*)(dst_o + 16 * mt + 4 * gq) = acc[mt] * inv;
+      if (gq == 0) *dst_l = l > 0.f ? (m_run + fast_log2(l)) * kLn2 : kNegInf;
+    }
     g = sg1;
   }
   if (bad) atomicOr(a.flags, kFlagBadBlock);
@@ -322,10 +334,10 @@ static int mla_cus(int device) {
   return cus;
 }
 
-int32_t mla_mfma_workers(int device, int32_t Hq, int32_t max_workers) {
+int32_t mla_mfma_workers(int device, int32_t Ru, int32_t max_workers) {
   // LDS (2 x 36.5 KB per workgroup) allows two resident workgroups per CU; registers allow
   // two waves per SIMD, so two workgroups fit while a workgroup has at most four waves.
-  const int nw = Hq / 16;
+  const int nw = Ru / 16;
   const int per_cu = nw <= 4 ? 2 : 1;
   int32_t p = mla_cus(device) * per_cu;
   return p < max_workers ? p : max_workers;
@@ -333,7 +345,7 @@ int32_t mla_mfma_workers(int device, int32_t Hq, int32_t max_workers) {
 
 hipError_t launch_mla_mfma(const AttnArgs& a, hipStream_t stream) {
   const char* zr = a.zero_row;
-  switch (a.Hq / 16) {
+  switch (a.Ru / 16) {
     case 1: hipLaunchKernelGGL((mla_mfma_kernel<1>), dim3(a.P), dim3(64), 0, stream, a, zr); break;
     case 2: hipLaunchKernelGGL((mla_mfma_kernel<2>), dim3(a.P), dim3(128), 0, stream, a, zr); break;
     case 4: hipLaunchKernelGGL((mla_mfma_kernel<4>), dim3(a.P), dim3(256), 0, stream, a, zr); break;

@@ -45,7 +45,7 @@ __global__ void __launch_bounds__(kSchedThreads)
 schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_t units_per_bs,
                 int32_t P, int32_t* __restrict__ fin, int32_t bs, int32_t max_blocks,
                 int32_t* __restrict__ ubounds, int32_t* __restrict__ pre,
-                int32_t* __restrict__ flags) {
+                int32_t* __restrict__ flags, int32_t Tq, int32_t* __restrict__ qend) {
   __shared__ int32_t warp_sums[kSchedThreads / 64];
   __shared__ int32_t carry;
   __shared__ int32_t flag_acc;
@@ -104,7 +104,13 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
   }
   if (my_flag) atomicOr(&flag_acc, my_flag);
   if (tid == 0) pre[U] = carry;
-  __syncthreads();  // pre[] is complete and visible to the workgroup
+  __syncthreads();  // pre[] and ubounds[] are complete and visible to the workgroup
+  // position of each request's first query token: the end of its ranges minus Tq
+  for (int64_t b = tid; b < B; b += kSchedThreads) {
+    int32_t end = 0;
+    for (int32_t sh = 0; sh < S; ++sh) end = max(end, ubounds[2 * (b * S + sh) + 1]);
+    qend[b] = end - Tq;
+  }
   const int64_t T = carry;
   for (int64_t u = tid; u < U; u += kSchedThreads) {
     const int64_t p0 = pre[u], p1 = pre[u + 1];
@@ -126,9 +132,10 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
 
 hipError_t launch_schedule(const int32_t* bounds, int32_t B, int32_t S, int32_t units_per_bs,
                            int32_t P, int32_t* fin, int32_t bs, int32_t max_blocks,
-                           int32_t* ubounds, int32_t* pre, int32_t* flags, hipStream_t stream) {
+                           int32_t* ubounds, int32_t* pre, int32_t* flags, int32_t Tq,
+                           int32_t* qend, hipStream_t stream) {
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, bounds, B, S,
-                     units_per_bs, P, fin, bs, max_blocks, ubounds, pre, flags);
+                     units_per_bs, P, fin, bs, max_blocks, ubounds, pre, flags, Tq, qend);
   return hipGetLastError();
 }
 
@@ -138,30 +145,34 @@ hipError_t launch_schedule(const int32_t* bounds, int32_t B, int32_t S, int32_t 
 // O = 0, LSE = -inf. A unit cut by worker boundaries left one piece per covering worker
 // (none from a worker whose range is empty); the pieces are merged by the LSE formula.
 // Grid (x, c): workgroup x takes list entries x, x + gridDim.x, ...; chunk c is 1024
-// consecutive output floats of the unit (one float4 per thread).
+// consecutive floats of the unit's Ru x Dv rows (one float4 per thread), each written to its
+// query row of the partials.
 constexpr int kFinishThreads = 256;
 constexpr int kFinishMaxPieces = 4096;  // >= the most workers any launch uses
 
 __global__ void __launch_bounds__(kFinishThreads)
-finish_units_kernel(AttnArgs a, int32_t Hu) {
+finish_units_kernel(AttnArgs a) {
   __shared__ int32_t slots[kFinishMaxPieces];  // -1 for workers that own no pages
   const int32_t count = a.flags[1];
   const int64_t T = a.pre[a.U];
   const int32_t per_bs = a.U / (a.B * a.S);
+  const int32_t Hu = a.Ru;
   const int32_t n4 = Hu * a.Dv / 4;
   const int32_t i4 = blockIdx.y * kFinishThreads + threadIdx.x;
-  const int32_t h = 4 * i4 / a.Dv;
-  const bool head_start = (4 * i4) % a.Dv == 0;
+  const int32_t h = 4 * i4 / a.Dv;          // local row of the unit
+  const int32_t c4 = i4 - h * (a.Dv / 4);   // float4 within the row
   for (int32_t e = blockIdx.x; e < count; e += gridDim.x) {
     const i32x4 ent = *(const i32x4*)(a.fin + 4 * (int64_t)e);
     const int32_t u = ent[0], w0 = ent[1], w1 = ent[2];
     const int32_t bsi = u / per_bs, hsub = u % per_bs;
-    float* out_o = a.part_o + ((int64_t)bsi * a.Hq + (int64_t)hsub * Hu) * a.Dv;
-    float* out_l = a.part_lse + (int64_t)bsi * a.Hq + (int64_t)hsub * Hu;
+    int32_t jtok = 0;
+    const int32_t rho = (i4 < n4) ? unit_row(a, hsub / a.NRg, hsub % a.NRg, h, &jtok) : -1;
+    float* out_o = a.part_o + ((int64_t)bsi * a.R + (rho < 0 ? 0 : rho)) * a.Dv;
+    float* out_l = a.part_lse + (int64_t)bsi * a.R + (rho < 0 ? 0 : rho);
     if (w0 < 0) {
-      if (i4 < n4) {
-        ((f32x4*)out_o)[i4] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (head_start) out_l[h] = kNegInf;
+      if (rho >= 0) {
+        ((f32x4*)out_o)[c4] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (c4 == 0) *out_l = kNegInf;
       }
       continue;
     }
@@ -174,7 +185,7 @@ finish_units_kernel(AttnArgs a, int32_t Hu) {
       slots[k] = (worker_begin(T, a.P, w + 1) == wb) ? -1 : piece_slot(w, !(w == w0 && wb < p0));
     }
     __syncthreads();
-    if (i4 >= n4) continue;
+    if (rho < 0) continue;
     float m = kNegInf;
     for (int32_t k = 0; k < ns; ++k)
       if (slots[k] >= 0) m = fmaxf(m, a.piece_lse[(int64_t)slots[k] * Hu + h]);
@@ -189,20 +200,19 @@ finish_units_kernel(AttnArgs a, int32_t Hu) {
       acc += wt * o;
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    ((f32x4*)out_o)[i4] = acc * inv;
-    if (head_start) out_l[h] = den > 0.f ? m + logf(den) : kNegInf;
+    ((f32x4*)out_o)[c4] = acc * inv;
+    if (c4 == 0) *out_l = den > 0.f ? m + logf(den) : kNegInf;
   }
 }
 
-hipError_t launch_finish_units(const AttnArgs& a, int32_t Hu, hipStream_t stream) {
+hipError_t launch_finish_units(const AttnArgs& a, hipStream_t stream) {
   if (a.U == 0) return hipSuccess;
   if (a.P > kFinishMaxPieces) return hipErrorInvalidValue;
-  const int32_t n4 = Hu * a.Dv / 4;
+  const int32_t n4 = a.Ru * a.Dv / 4;
   const int32_t chunks = (n4 + kFinishThreads - 1) / kFinishThreads;
   int32_t x = (4096 + chunks - 1) / chunks;
   if (x > a.U) x = a.U;
-  hipLaunchKernelGGL(finish_units_kernel, dim3(x, chunks), dim3(kFinishThreads), 0, stream, a,
-                     Hu);
+  hipLaunchKernelGGL(finish_units_kernel, dim3(x, chunks), dim3(kFinishThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -298,7 +308,9 @@ hipError_t launch_debug_gather(const dcp_attn_shape& sh, const void* cache,
 // writes position L: slot L % bs of page block_table[b][L / bs]. Its owner is the shard whose
 // range in the plan of L + 1 tokens contains L: with p = L / bs that plan has p + 1 pages and
 // k = ceil((p + 1) / S) pages per shard, so the owner is p / k. Rows move as 16-byte chunks:
-// kc (and vc) chunks per head, Hkv heads (1 for the MLA latent cache, vc = 0).
+// kc (and vc) chunks per head, Hkv heads (1 for the MLA latent cache, vc = 0). The first
+// chunk of each thread is loaded before the length and the table entry are known, so its
+// latency overlaps theirs instead of following them.
 constexpr int32_t kAppendThreads = 128;
 
 __global__ void __launch_bounds__(kAppendThreads)
@@ -308,6 +320,17 @@ append_kv_kernel(const int32_t* __restrict__ seq_lens, const int32_t* __restrict
                  int32_t* __restrict__ owner, int32_t Hkv, int32_t kc, int32_t vc, int32_t bs,
                  int32_t max_blocks, int32_t num_blocks, int32_t S) {
   const int32_t b = blockIdx.x;
+  const int32_t per_head = kc + vc;
+  const int32_t total = Hkv * per_head;
+  auto src_of = [&](int32_t i) -> i32x4 {
+    const int32_t h = i / per_head, j = i - h * per_head;
+    const int64_t src = (int64_t)b * Hkv + h;
+    return j < kc ? new_k[src * kc + j] : new_v[src * vc + (j - kc)];
+  };
+  const int32_t i0 = threadIdx.x;
+  i32x4 first = {0, 0, 0, 0};
+  if (i0 < total) first = src_of(i0);
+
   const int32_t L = seq_lens[b];
   const int32_t p = L >= 0 ? L / bs : 0;
   int32_t who = -1;
@@ -317,23 +340,23 @@ append_kv_kernel(const int32_t* __restrict__ seq_lens, const int32_t* __restrict
     if (blk < 0 || blk >= num_blocks) {
       who = -2;
     } else {
-      const int64_t per_shard = ((int64_t)p + S) / S;
-      who = (int32_t)(p / per_shard);
+      const uint32_t per_shard = ((uint32_t)p + (uint32_t)S) / (uint32_t)S;  // < 2^32: p, S < 2^31
+      who = (int32_t)((uint32_t)p / per_shard);
     }
   }
   if (owner && threadIdx.x == 0) owner[b] = who;
   if (who < 0) return;
   const int32_t slot = L - p * bs;
-  const int32_t per_head = kc + vc;
-  for (int32_t i = threadIdx.x; i < Hkv * per_head; i += kAppendThreads) {
+  auto store = [&](int32_t i, i32x4 val) {
     const int32_t h = i / per_head, j = i - h * per_head;
     const int64_t row = ((int64_t)blk * Hkv + h) * bs + slot;
-    const int64_t src = (int64_t)b * Hkv + h;
     if (j < kc)
-      k_cache[row * kc + j] = new_k[src * kc + j];
+      k_cache[row * kc + j] = val;
     else
-      v_cache[row * vc + (j - kc)] = new_v[src * vc + (j - kc)];
-  }
+      v_cache[row * vc + (j - kc)] = val;
+  };
+  if (i0 < total) store(i0, first);
+  for (int32_t i = i0 + kAppendThreads; i < total; i += kAppendThreads) store(i, src_of(i));
 }
 
 hipError_t launch_append_kv(const dcp_attn_shape& sh, const int32_t* seq_lens,

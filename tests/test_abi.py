@@ -24,7 +24,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = dcp.load()
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(dcp.EXPORTS) == names
@@ -184,3 +184,23 @@ def test_append_error_paths_return_before_device_work():
     assert call(gqa, nv=A + 4, vc=A) == dcp.DCP_ERR_ALIGN
     gqa_odd = _shape(kind="gqa", num_q_heads=8, num_kv_heads=2, head_dim_qk=4, head_dim_v=4)
     assert call(gqa_odd, nv=A, vc=A) == dcp.DCP_ERR_UNSUPPORTED
+
+
+def test_multi_token_shapes_and_errors():
+    sh = _shape()
+    one = dcp.dcp_workspace_bytes(sh)
+    assert dcp.dcp_workspace_bytes_multi(sh, 1) == one
+    assert dcp.dcp_workspace_bytes_multi(sh, 4) > one
+    for bad in (0, 17, -1):
+        with pytest.raises(dcp.DcpError) as e:
+            dcp.dcp_workspace_bytes_multi(sh, bad)
+        assert e.value.status == dcp.DCP_ERR_SHAPE
+    lib = dcp.load()
+    A = 0x10000
+    need = dcp.dcp_workspace_bytes_multi(sh, 3)
+    assert lib.dcp_decode_attn_multi(ctypes.byref(sh), 3, A, A, None, A, A, A, need - 1, A, None,
+                                     None) == dcp.DCP_ERR_WORKSPACE
+    assert lib.dcp_decode_attn_multi(ctypes.byref(sh), 0, A, A, None, A, A, A, need, A, None,
+                                     None) == dcp.DCP_ERR_SHAPE
+    assert lib.dcp_decode_attn_multi_partial(ctypes.byref(sh), 2, A, A, None, A, A, None, A, A,
+                                             need, None) == dcp.DCP_ERR_NULL

@@ -1,0 +1,113 @@
+"""GPU parity of several query tokens per request (causal rows) against the float64 oracle:
+partials, the merge and the fused call, for MLA and both GQA kernels, with row counts that
+fit one unit, that need several row groups and that leave padding rows; requests shorter
+than q_len; and q_len = 1 through the multi-token calls against the one-token calls."""
+
+import numpy as np
+import pytest
+import torch
+
+import sequence_sharded_kv_amd as dcp
+from gpu_helpers import assert_close, host_inputs_of, say, shape_of, to_device
+from oracle import oracle as O
+from workloads import make_host_inputs, make_queries, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _q_device(wl, qh):
+    if qh.dtype == np.uint16:
+        return torch.from_numpy(qh.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(qh).cuda()
+
+
+# name, workload, lengths, q_len, overrides
+CASES = [
+    ("mla-64h-t2", "mla-64h-b512", [2000, 1, 700], 2, dict(batch=3)),
+    ("mla-64h-t3-two-groups", "mla-64h-b512", [1500, 64, 2], 3, dict(batch=3)),
+    ("mla-16h-t8", "mla-64h-b512", [900, 8, 3], 8, dict(batch=3, num_q_heads=16)),
+    ("mla-128h-t2", "mla-128h", [1200, 33], 2, dict(batch=2)),
+    ("mla-32h-t3-padding", "mla-64h-b512", [600, 97], 3, dict(batch=2, num_q_heads=32)),
+    ("mla-64h-t4-bs1", "mla-64h-b512", [150, 5], 4, dict(batch=2, block_size=1)),
+    ("gqa-g16-t2", "gqa-g16", [3000, 1, 100], 2, dict(batch=3)),
+    ("gqa-g4-d64-t4", "gqa-g16", [900, 3], 4, dict(batch=2, num_q_heads=16, head_dim_qk=64,
+                                                    head_dim_v=64)),
+    ("gqa-g8-t3-S16", "gqa-long", [5000, 40], 3, dict(batch=2, plants_per_head=0)),
+    ("gqa-f32-valu-t2", "gqa-g16", [1100, 2], 2, dict(batch=2, dtype="f32")),
+    ("gqa-d256-valu-t3", "gqa-g16", [700, 70], 3, dict(batch=2, head_dim_qk=256,
+                                                      head_dim_v=256)),
+    ("gqa-g16-t5-bs24", "gqa-g16", [500, 49], 5, dict(batch=2, block_size=24)),
+]
+
+
+@pytest.mark.parametrize("name,wl_name,lengths,T,over", CASES, ids=[c[0] for c in CASES])
+def test_multi_token_partials_and_fused_match_oracle(name, wl_name, lengths, T, over):
+    say(f"[gpu] multi-token case {name} (q_len {T})")
+    wl = workload(wl_name).replace(**over)
+    if wl.length_law == "fixed":
+        wl = wl.replace(lengths=tuple(lengths))
+    host = make_host_inputs(wl, lengths=lengths)
+    inp = to_device(wl, host)
+    qh = make_queries(wl, T)
+    q = _q_device(wl, qh)
+    sh = shape_of(wl, inp)
+    B, S, Hq, Dv = wl.batch, wl.num_shards, wl.num_q_heads, wl.head_dim_v
+    bounds_np = dcp.dcp_plan_shards(host["seq_lens"], S, wl.block_size)
+    bounds = torch.from_numpy(bounds_np).cuda()
+    ws = dcp.alloc_workspace(sh, "cuda", T)
+    k = inp["kv_cache"] if wl.kind == "mla" else inp["k_cache"]
+    v = None if wl.kind == "mla" else inp["v_cache"]
+    po = torch.empty((B, S, T, Hq, Dv), dtype=torch.float32, device="cuda")
+    pl = torch.empty((B, S, T, Hq), dtype=torch.float32, device="cuda")
+    dcp.dcp_decode_attn_multi_partial(sh, T, q, k, v, inp["block_table"], bounds, po, pl, ws)
+    out = torch.empty((B, T, Hq, Dv), dtype=torch.float32, device="cuda")
+    out_lse = torch.empty((B, T, Hq), dtype=torch.float32, device="cuda")
+    dcp.dcp_decode_attn_multi(sh, T, q, k, v, inp["block_table"], bounds, ws, out, out_lse)
+    mo = torch.empty_like(out)
+    ml = torch.empty_like(out_lse)
+    dcp.dcp_merge_lse(po.view(B, S, T * Hq, Dv), pl.view(B, S, T * Hq), mo.view(B, T * Hq, Dv),
+                      ml.view(B, T * Hq))
+    torch.cuda.synchronize()
+    assert dcp.dcp_read_device_flags(ws) == 0
+    _, caches, bt, _ = host_inputs_of(wl, inp)
+    ro, rl = O.partial_attention_multi(wl.kind, wl.dtype, qh, caches, bt,
+                                       np.asarray(bounds_np, np.int64), wl.block_size,
+                                       wl.softmax_scale, Dv)
+    assert_close(po.cpu().numpy().reshape(B, S, T * Hq, Dv), pl.cpu().numpy().reshape(B, S, T * Hq),
+                 ro.reshape(B, S, T * Hq, Dv), rl.reshape(B, S, T * Hq), wl.dtype,
+                 f"{name} partials")
+    fo, fl = O.merge_lse(ro.reshape(B, S, T * Hq, Dv), rl.reshape(B, S, T * Hq))
+    assert_close(out.cpu().numpy().reshape(B, T * Hq, Dv), out_lse.cpu().numpy().reshape(B, T * Hq),
+                 fo, fl, wl.dtype, f"{name} fused")
+    assert_close(mo.cpu().numpy().reshape(B, T * Hq, Dv), ml.cpu().numpy().reshape(B, T * Hq),
+                 fo, fl, wl.dtype, f"{name} merged")
+    # a request shorter than q_len: its first tokens see nothing at all
+    for b, L in enumerate(lengths):
+        for j in range(T):
+            if L - T + j + 1 <= 0:
+                assert torch.all(out[b, j] == 0) and torch.all(torch.isneginf(out_lse[b, j]))
+
+
+@pytest.mark.parametrize("wl_name,over,lengths", [
+    ("mla-64h-b512", dict(batch=3), [1000, 77, 1]),
+    ("gqa-g16", dict(batch=3), [2000, 50, 0]),
+])
+def test_multi_with_one_token_equals_one_token_calls(wl_name, over, lengths):
+    """q_len = 1 through the multi-token calls gives the one-token calls' bits."""
+    say(f"[gpu] q_len 1 through the multi-token calls: {wl_name}")
+    wl = workload(wl_name).replace(**over)
+    host = make_host_inputs(wl, lengths=lengths)
+    inp = to_device(wl, host)
+    sh = shape_of(wl, inp)
+    bounds = torch.from_numpy(dcp.dcp_plan_shards(host["seq_lens"], wl.num_shards,
+                                                  wl.block_size)).cuda()
+    ws = dcp.alloc_workspace(sh, "cuda")
+    k = inp["kv_cache"] if wl.kind == "mla" else inp["k_cache"]
+    v = None if wl.kind == "mla" else inp["v_cache"]
+    o1 = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim_v), dtype=torch.float32, device="cuda")
+    l1 = torch.empty((wl.batch, wl.num_q_heads), dtype=torch.float32, device="cuda")
+    dcp.dcp_decode_attn(sh, inp["q"], k, v, inp["block_table"], bounds, ws, o1, l1)
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    dcp.dcp_decode_attn_multi(sh, 1, inp["q"], k, v, inp["block_table"], bounds, ws, o2, l2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

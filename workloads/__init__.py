@@ -1,9 +1,10 @@
 """Seeded synthetic inputs for sequence-sharded paged decode attention.
 
 This package only draws inputs (context lengths, page pools and block tables,
-queries, KV caches, planted keys, the rows of newly decoded tokens). It holds
-none of the attention arithmetic, no shard plan and no kernel logic; the CPU
-oracle and the GPU path both consume what it produces.
+queries of one or several tokens, KV caches, planted keys, the rows of newly
+decoded tokens). It holds none of the attention arithmetic, no shard plan and
+no kernel logic; the CPU oracle and the GPU path both consume what it
+produces.
 """
 
 from .configs import (  # noqa: F401
@@ -15,5 +16,6 @@ from .configs import (  # noqa: F401
     make_device_inputs,
     make_host_inputs,
     make_new_rows,
+    make_queries,
     workload,
 )

@@ -231,6 +231,18 @@ def make_host_inputs(wl: Workload, seed: Optional[int] = None, lengths=None, max
     return out
 
 
+def make_queries(wl: Workload, q_len: int, seed: Optional[int] = None,
+                 batch: Optional[int] = None) -> np.ndarray:
+    """Queries of q_len tokens per request, [B, q_len, Hq, Dqk], drawn like the one-token
+    queries (bf16 as uint16 bit patterns, f32 as float32)."""
+    B = wl.batch if batch is None else batch
+    rng = np.random.default_rng(np.random.SeedSequence(3000 + wl.seed_index if seed is None
+                                                       else seed))
+    q = rng.standard_normal((B, q_len, wl.num_q_heads, wl.head_dim_qk),
+                            dtype=np.float32) * _std_vector(wl)
+    return bf16_bits_from_f32(q) if wl.dtype == "bf16" else q
+
+
 def make_new_rows(wl: Workload, seed: Optional[int] = None, batch: Optional[int] = None):
     """Rows of the token each request decodes this step, drawn like the cache rows.
 
