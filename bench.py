@@ -10,6 +10,8 @@ lognormal contexts with median 67K tokens, 64-token pages, 8 contiguous shards p
 Prints one JSON line: the whole-step algorithmic HBM throughput (TB/s) as `value`, decode
 steps/s, the dominant kernel's roofline (its own launch time from HIP events recorded by
 the library on the launch stream) and the float64 CPU oracle timed on a bounded sample.
+With --q-len T > 1 a step scores T query tokens per request (dcp_decode_attn_multi, causal
+rows) over the same cache; the KV bytes are still counted once.
 """
 
 from __future__ import annotations
@@ -46,6 +48,8 @@ def parse_args():
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mla-64h-b512")
+    p.add_argument("--q-len", type=int, default=1,
+                   help="query tokens per request (speculative / MTP decode); 1 = plain decode")
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -71,18 +75,20 @@ def kernel_family(wl):
     return "gqa-valu"
 
 
-def byte_model(wl, lens):
-    """Algorithmic bytes of one step: what the method must move at least once."""
+def byte_model(wl, lens, q_len=1):
+    """Algorithmic bytes of one step: what the method must move at least once (the KV once,
+    whatever the number of query tokens)."""
     esz = 2 if wl.dtype == "bf16" else 4
     tokens = int(np.sum(lens))
     if wl.kind == "mla":
         kv = tokens * wl.head_dim_qk * esz                      # V shares the latent bytes
     else:
         kv = tokens * wl.num_kv_heads * wl.head_dim_qk * esz * 2
-    q = wl.batch * wl.num_q_heads * wl.head_dim_qk * esz
+    rows = q_len * wl.num_q_heads
+    q = wl.batch * rows * wl.head_dim_qk * esz
     table = int(np.sum(-(-np.asarray(lens, np.int64) // wl.block_size))) * 4
-    part = wl.batch * wl.num_shards * wl.num_q_heads * (wl.head_dim_v + 1) * 4
-    out = wl.batch * wl.num_q_heads * (wl.head_dim_v + 1) * 4
+    part = wl.batch * wl.num_shards * rows * (wl.head_dim_v + 1) * 4
+    out = wl.batch * rows * (wl.head_dim_v + 1) * 4
     return {"kv": kv, "q": q, "table": table, "partials_rw": 2 * part, "out": out,
             "step": kv + q + table + 2 * part + out,
             "partial_kernel": kv + q + table + part, "tokens": tokens}
@@ -197,10 +203,12 @@ def cpu_baseline(wl, inp, bounds_np, seconds):
 
 # ------------------------------------------------------------------ main
 
-def time_append(wl, sh, inp, k_cache, v_cache, dev, n):
+def time_append(wl, sh, inp, k_cache, v_cache, dev, n, busy):
     """Time dcp_append_kv storing one new row per request (after the attention timing, so the
     attention inputs are untouched while they are measured). Each request rewrites the slot
-    of its last cached token, which its block table always covers."""
+    of its last cached token, which its block table always covers. `busy` queues one
+    attention step first: while the GPU runs it, the host queues all n appends, so the
+    events between them time back-to-back launches rather than the host's call rate."""
     import torch
     import sequence_sharded_kv_amd as dcp
     from workloads import make_new_rows
@@ -222,6 +230,7 @@ def time_append(wl, sh, inp, k_cache, v_cache, dev, n):
     torch.cuda.synchronize()
     assert int(owner.min()) >= 0
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    busy()
     a.record()
     for _ in range(n):
         call()
@@ -234,7 +243,7 @@ def time_append(wl, sh, inp, k_cache, v_cache, dev, n):
     nbytes = wl.batch * (2 * row + 3 * 4)   # new rows read, cache rows written, len/table/owner
     return {"us_per_launch": round(us, 3), "launches": n, "algorithmic_bytes": nbytes,
             "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
-            "bound": "launch latency (one row per request)"}
+            "bound": "launch latency (one row per request, launches queued back to back)"}
 
 
 def main():
@@ -268,9 +277,19 @@ def main():
                         wl.head_dim_qk, wl.head_dim_v, wl.block_size,
                         int(inp["block_table_host"].shape[1]), int(inp["num_blocks"]),
                         wl.num_shards, wl.softmax_scale)
-    ws = dcp.alloc_workspace(sh, dev)
-    out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim_v), dtype=torch.float32, device=dev)
-    out_lse = torch.empty((wl.batch, wl.num_q_heads), dtype=torch.float32, device=dev)
+    T = args.q_len
+    ws = dcp.alloc_workspace(sh, dev, T)
+    out = torch.empty((wl.batch, T, wl.num_q_heads, wl.head_dim_v), dtype=torch.float32,
+                      device=dev)
+    out_lse = torch.empty((wl.batch, T, wl.num_q_heads), dtype=torch.float32, device=dev)
+    if T > 1:
+        from workloads import make_queries
+        qh = make_queries(wl, T, seed=args.seed)
+        q_dev = torch.from_numpy(qh.view(np.int16) if qh.dtype == np.uint16 else qh).to(dev)
+        if qh.dtype == np.uint16:
+            q_dev = q_dev.view(torch.bfloat16)
+    else:
+        q_dev = inp["q"]
     k_cache = inp["kv_cache"] if wl.kind == "mla" else inp["k_cache"]
     v_cache = None if wl.kind == "mla" else inp["v_cache"]
     torch.cuda.synchronize()
@@ -278,8 +297,12 @@ def main():
           f"{int(lens.sum())} tokens", file=sys.stderr, flush=True)
 
     def step():
-        dcp.dcp_decode_attn(sh, inp["q"], k_cache, v_cache, inp["block_table"], bounds, ws, out,
-                            out_lse)
+        if T == 1:
+            dcp.dcp_decode_attn(sh, q_dev, k_cache, v_cache, inp["block_table"], bounds, ws, out,
+                                out_lse)
+        else:
+            dcp.dcp_decode_attn_multi(sh, T, q_dev, k_cache, v_cache, inp["block_table"], bounds,
+                                      ws, out, out_lse)
 
     if args.calibration_copy_gib > 0:
         n = int(args.calibration_copy_gib * (1 << 30) // 4)
@@ -307,19 +330,19 @@ def main():
     launches, kernel_ms = dcp.dcp_kernel_timing_end()
     per_step = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     ms_per_step = (t1 - t0) * 1e3 / K
-    bm = byte_model(wl, lens)
+    bm = byte_model(wl, lens, T)
     value = bm["step"] / (ms_per_step * 1e-3) / 1e12
     kern_avg_ms = kernel_ms / max(launches, 1)
     achieved = bm["partial_kernel"] / (kern_avg_ms * 1e-3) / 1e9
-    traffic = load_traffic(wl.name, family)
+    traffic = load_traffic(wl.name, family) if T == 1 else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else int(traffic["traffic_bytes_per_launch"]),
                 "kernel": KERNEL_NAMES[family], "kernel_avg_ms": round(kern_avg_ms, 4),
                 "algorithmic_bytes_per_launch": int(bm["partial_kernel"])}
-    append = time_append(wl, sh, inp, k_cache, v_cache, dev, max(K, 20))
+    append = time_append(wl, sh, inp, k_cache, v_cache, dev, 200, step)
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and T == 1:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, inp, bounds_np, args.cpu_seconds)
     q = np.percentile(per_step, [10, 50, 90])
@@ -332,7 +355,8 @@ def main():
         "steps_per_s": round(1e3 / ms_per_step, 2),
         "pct_of_hbm_peak": round(100 * value * 1e3 / HBM_PEAK_GBS, 2),
         "ms_per_step_p10_p50_p90": [round(float(x), 4) for x in q],
-        "config": {"workload": wl.name, "kind": wl.kind, "batch": wl.batch,
+        "config": {"workload": wl.name if T == 1 else f"{wl.name}-q{T}", "kind": wl.kind,
+                   "batch": wl.batch, "query_tokens": T,
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
                    "head_dim_qk": wl.head_dim_qk, "head_dim_v": wl.head_dim_v,
                    "block_size": wl.block_size, "num_shards": wl.num_shards,
