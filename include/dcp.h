@@ -216,7 +216,10 @@ dcp_status dcp_decode_attn_multi(const dcp_attn_shape* shape, int32_t q_len, con
  * dcp_read_device_flags -- copy the sticky device-side flag word out of a workspace and
  * wait for `stream`. Bit 0: a bound was clamped into [0, max_blocks_per_seq*block_size] or
  * had end < start. Bit 1: a block id outside [0, num_blocks) was met and its tokens masked.
- * Bits are cleared by the next dcp_decode_attn[_partial] call on that workspace.
+ * Bit 2 (informational, results unaffected): on the MLA path with 128 query rows per unit, a
+ * score exceeded its segment's first-tile maximum by more than 2^64 in weight, and that
+ * worker's range was recomputed by the general kernel. Bits are cleared by the next
+ * attention call on that workspace.
  */
 dcp_status dcp_read_device_flags(const void* workspace, int32_t* flags, void* stream);
 

@@ -152,6 +152,7 @@ dcp_status make_plan(const dcp_attn_shape* sh, int32_t Tq, dcp::Plan* plan) {
   w.fin = off;         off = align_up(off + sizeof(int32_t) * 4 * (size_t)units);
   w.ubounds = off;     off = align_up(off + sizeof(int32_t) * B * S * 2);
   w.qend = off;        off = align_up(off + sizeof(int32_t) * B);
+  w.redo = off;        off = align_up(off + sizeof(int32_t) * (size_t)pmax);
   w.piece_o = off;     off = align_up(off + sizeof(float) * 2 * (size_t)pmax * ru * Dv);
   w.piece_lse = off;   off = align_up(off + sizeof(float) * 2 * (size_t)pmax * ru);
   w.part_o = off;      off = align_up(off + sizeof(float) * B * S * R * Dv);
@@ -200,6 +201,7 @@ dcp_status run_partials(const dcp_attn_shape* sh, int32_t Tq, const void* q, con
   a.pre = reinterpret_cast<int32_t*>(ws + plan.ws.pre);
   a.fin = reinterpret_cast<int32_t*>(ws + plan.ws.fin);
   a.qend = reinterpret_cast<int32_t*>(ws + plan.ws.qend);
+  a.redo = reinterpret_cast<int32_t*>(ws + plan.ws.redo);
   a.part_o = fused ? reinterpret_cast<float*>(ws + plan.ws.part_o) : part_o;
   a.part_lse = fused ? reinterpret_cast<float*>(ws + plan.ws.part_lse) : part_lse;
   a.piece_o = reinterpret_cast<float*>(ws + plan.ws.piece_o);
@@ -233,7 +235,7 @@ dcp_status run_partials(const dcp_attn_shape* sh, int32_t Tq, const void* q, con
   e = dcp::launch_schedule(bounds, a.B, a.S, units_per_bs, a.P,
                            reinterpret_cast<int32_t*>(ws + plan.ws.fin), a.bs, a.max_blocks,
                            const_cast<int32_t*>(a.ubounds), const_cast<int32_t*>(a.pre), a.flags,
-                           Tq, const_cast<int32_t*>(a.qend), s);
+                           Tq, const_cast<int32_t*>(a.qend), a.redo, s);
   if (e != hipSuccess) return device_fail(e, "schedule launch");
   const bool timed = g_timing.on && g_timing.used < g_timing.start.size();
   if (timed) {

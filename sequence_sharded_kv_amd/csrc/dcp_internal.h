@@ -17,6 +17,7 @@ constexpr int32_t kWsZeroWords = 512;  // 2 KB of zeros
 // Flag bits in the workspace's sticky device flag word.
 constexpr int32_t kFlagBoundClamped = 1;
 constexpr int32_t kFlagBadBlock = 2;
+constexpr int32_t kFlagRecomputed = 4;  // a worker's range was recomputed (see mla_wide_kernel)
 
 // Work is split stream-K style: every (unit, page) pair is one page of work, the pages of
 // all units are concatenated in unit order, and worker w takes the contiguous range
@@ -42,12 +43,13 @@ constexpr int32_t kFlagBadBlock = 2;
 //                                for units with no pages; unordered
 //   ubounds    int32[B*S*2]      sanitised (start, end) per (request, shard)
 //   qend       int32[B]          position of each request's first query token
+//   redo       int32[Pmax]       workers a kernel marked for recomputation
 //   piece_o    float[2*Pmax][Ru][Dv]
 //   piece_lse  float[2*Pmax][Ru]
 //   part_o     float[B][S][R][Dv]    (fused path only)
 //   part_lse   float[B][S][R]
 struct WsLayout {
-  size_t flags, pre, fin, ubounds, qend, piece_o, piece_lse, part_o, part_lse, total;
+  size_t flags, pre, fin, ubounds, qend, redo, piece_o, piece_lse, part_o, part_lse, total;
 };
 
 enum class Kernel { kNone = 0, kGqaValu, kGqaMfma, kMlaMfma };
@@ -76,6 +78,7 @@ struct AttnArgs {
   float* piece_o;           // [2P][Ru][Dv]
   float* piece_lse;         // [2P][Ru]
   int32_t* flags;
+  int32_t* redo;            // [P] workers to recompute (cleared by the schedule kernel)
   const char* zero_row;     // kWsZeroWords*4 bytes of zeros in the workspace
   int32_t B, S, Hq, Hkv, G, Dqk, Dv, bs, max_blocks, num_blocks, U, P;
   int32_t Tq, R, Ru, NRg;   // query tokens, rows per request, rows per unit, groups per KV head
@@ -98,7 +101,8 @@ hipError_t launch_plan_device(const int32_t* seq_lens, int32_t B, int32_t S, int
 hipError_t launch_schedule(const int32_t* bounds, int32_t B, int32_t S, int32_t units_per_bs,
                            int32_t P, int32_t* fin,
                            int32_t bs, int32_t max_blocks, int32_t* ubounds, int32_t* pre,
-                           int32_t* flags, int32_t Tq, int32_t* qend, hipStream_t stream);
+                           int32_t* flags, int32_t Tq, int32_t* qend, int32_t* redo,
+                           hipStream_t stream);
 hipError_t launch_finish_units(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_merge(int32_t B, int32_t S, int32_t H, int32_t Dv, const float* part_o,
                         const float* part_lse, float* out, float* out_lse, hipStream_t stream);

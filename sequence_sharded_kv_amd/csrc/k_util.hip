@@ -38,14 +38,15 @@ hipError_t launch_plan_device(const int32_t* seq_lens, int32_t B, int32_t S, int
 // write the exclusive prefix sum pre[0..U] (units ordered (b, s, h) with h < units_per_bs).
 // A second pass lists the units the finishing pass must write (cut by a worker boundary, or
 // without pages) in `fin`, with their count in flags[1]. Also clears the flag word (the
-// first call of a step owns it).
+// first call of a step owns it) and the P recomputation marks.
 constexpr int kSchedThreads = 1024;
 
 __global__ void __launch_bounds__(kSchedThreads)
 schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_t units_per_bs,
                 int32_t P, int32_t* __restrict__ fin, int32_t bs, int32_t max_blocks,
                 int32_t* __restrict__ ubounds, int32_t* __restrict__ pre,
-                int32_t* __restrict__ flags, int32_t Tq, int32_t* __restrict__ qend) {
+                int32_t* __restrict__ flags, int32_t Tq, int32_t* __restrict__ qend,
+                int32_t* __restrict__ redo) {
   __shared__ int32_t warp_sums[kSchedThreads / 64];
   __shared__ int32_t carry;
   __shared__ int32_t flag_acc;
@@ -53,6 +54,7 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
   const int tid = threadIdx.x;
   if (tid == 0) { carry = 0; flag_acc = 0; fin_count = 0; }
   for (int i = tid; i < kWsZeroWords; i += kSchedThreads) flags[kWsZeroOffset / 4 + i] = 0;
+  for (int i = tid; i < P; i += kSchedThreads) redo[i] = 0;
   __syncthreads();
   const int64_t cap = (int64_t)max_blocks * bs;
   const int64_t nbs = (int64_t)B * S;
@@ -133,9 +135,9 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
 hipError_t launch_schedule(const int32_t* bounds, int32_t B, int32_t S, int32_t units_per_bs,
                            int32_t P, int32_t* fin, int32_t bs, int32_t max_blocks,
                            int32_t* ubounds, int32_t* pre, int32_t* flags, int32_t Tq,
-                           int32_t* qend, hipStream_t stream) {
+                           int32_t* qend, int32_t* redo, hipStream_t stream) {
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, bounds, B, S,
-                     units_per_bs, P, fin, bs, max_blocks, ubounds, pre, flags, Tq, qend);
+                     units_per_bs, P, fin, bs, max_blocks, ubounds, pre, flags, Tq, qend, redo);
   return hipGetLastError();
 }
 

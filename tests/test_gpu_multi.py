@@ -111,3 +111,40 @@ def test_multi_with_one_token_equals_one_token_calls(wl_name, over, lengths):
     dcp.dcp_decode_attn_multi(sh, 1, inp["q"], k, v, inp["block_table"], bounds, ws, o2, l2)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_wide_mla_recomputes_workers_whose_scores_outrun_the_first_tile():
+    """128 query rows per unit take the 32-rows-per-wave kernel, whose weights are relative
+    to each segment's first-tile maximum. Two keys planted mid-shard score about 90 (natural
+    log units) above the rest, so those workers are recomputed by the general kernel: the
+    result still matches the oracle and flag bit 2 reports the recomputation."""
+    from workloads import bf16_bits_from_f32
+    say("[gpu] wide MLA kernel with planted high-score keys")
+    wl = workload("mla-128h").replace(batch=2)
+    lengths = [3000, 2000]
+    host = make_host_inputs(wl, lengths=lengths)
+    bs = wl.block_size
+    q0 = (host["q"][0, 0].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    c = 90.0 / (wl.softmax_scale * float(q0 @ q0))
+    key = bf16_bits_from_f32((c * q0).astype(np.float32))
+    # positions in the second half of their 64-token page: with this little work every
+    # non-empty worker covers one page, so the plant is past each segment's first tile
+    for t in (2536, 1330):
+        host["kv_cache"][host["block_table"][0, t // bs], t % bs] = key
+    inp = to_device(wl, host)
+    sh = shape_of(wl, inp)
+    bounds_np = dcp.dcp_plan_shards(host["seq_lens"], wl.num_shards, bs)
+    bounds = torch.from_numpy(bounds_np).cuda()
+    ws = dcp.alloc_workspace(sh, "cuda")
+    out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim_v), dtype=torch.float32,
+                      device="cuda")
+    out_lse = torch.empty((wl.batch, wl.num_q_heads), dtype=torch.float32, device="cuda")
+    dcp.dcp_decode_attn(sh, inp["q"], inp["kv_cache"], None, inp["block_table"], bounds, ws, out,
+                        out_lse)
+    torch.cuda.synchronize()
+    assert dcp.dcp_read_device_flags(ws) == 4
+    hq, caches, bt, lens = host_inputs_of(wl, inp)
+    fo, fl = O.full_attention("mla", wl.dtype, hq, caches, bt, lens, bs, wl.softmax_scale,
+                              wl.head_dim_v)
+    assert float(np.max(fl[0])) > 80.0
+    assert_close(out.cpu().numpy(), out_lse.cpu().numpy(), fo, fl, wl.dtype, "planted wide")
