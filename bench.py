@@ -35,11 +35,12 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "mla": ["k_mla_mfma.hip", "device_common.h", "dcp_internal.h"],
+    "mla-wide": ["k_mla_mfma.hip", "device_common.h", "dcp_internal.h"],
     "gqa-mfma": ["k_gqa_mfma.hip", "device_common.h", "dcp_internal.h"],
     "gqa-valu": ["k_gqa_valu.hip", "device_common.h", "dcp_internal.h"],
 }
-KERNEL_NAMES = {"mla": "mla_mfma_kernel", "gqa-mfma": "gqa_mfma_kernel",
-                "gqa-valu": "gqa_valu_kernel"}
+KERNEL_NAMES = {"mla": "mla_mfma_kernel", "mla-wide": "mla_wide_kernel",
+                "gqa-mfma": "gqa_mfma_kernel", "gqa-valu": "gqa_valu_kernel"}
 
 
 def parse_args():
@@ -66,9 +67,11 @@ def parse_args():
 
 # ------------------------------------------------------------------ byte model
 
-def kernel_family(wl):
+def kernel_family(wl, q_len=1):
     if wl.kind == "mla":
-        return "mla"
+        # more than 64 query rows per unit take the 32-rows-per-wave kernel (32 | Hq)
+        rows = q_len * wl.num_q_heads
+        return "mla-wide" if rows > 64 and wl.num_q_heads % 32 == 0 else "mla"
     g = wl.num_q_heads // wl.num_kv_heads
     if wl.dtype == "bf16" and g <= 16 and wl.head_dim_qk in (64, 128):
         return "gqa-mfma"
@@ -250,7 +253,7 @@ def main():
     args = parse_args()
     from workloads import make_device_inputs, workload
     wl = workload(args.workload)
-    family = kernel_family(wl)
+    family = kernel_family(wl, args.q_len)
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(*args.summarize_pmc, args.workload, family,
                                        args.pmc_calibration_gib), indent=1))
