@@ -11,7 +11,9 @@ Prints one JSON line: the whole-step algorithmic HBM throughput (TB/s) as `value
 steps/s, the dominant kernel's roofline (its own launch time from HIP events recorded by
 the library on the launch stream) and the float64 CPU oracle timed on a bounded sample.
 With --q-len T > 1 a step scores T query tokens per request (dcp_decode_attn_multi, causal
-rows) over the same cache; the KV bytes are still counted once.
+rows) over the same cache; the KV bytes are still counted once. T > 16 is a prefill chunk
+(e.g. --workload mla-prefill --q-len 512): `value` and the roofline are then algorithmic
+TFLOP/s against the dense bf16 MFMA peak.
 """
 
 from __future__ import annotations
@@ -95,6 +97,20 @@ def byte_model(wl, lens, q_len=1):
     return {"kv": kv, "q": q, "table": table, "partials_rw": 2 * part, "out": out,
             "step": kv + q + table + 2 * part + out,
             "partial_kernel": kv + q + table + part, "tokens": tokens}
+
+
+def flop_model(wl, lens, q_len):
+    """Algorithmic flops of a step of q_len causal query tokens per request: every (row, visible
+    token) pair costs 2 Dqk (score) + 2 Dv (value) flops."""
+    per = 2 * wl.head_dim_qk + 2 * wl.head_dim_v
+    vis = 0
+    for L in np.asarray(lens, np.int64):
+        j = np.arange(q_len, dtype=np.int64)
+        vis += int(np.maximum(0, int(L) - q_len + j + 1).sum())
+    return vis * wl.num_q_heads * per
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 
 
 def sources_sha(family):
@@ -343,20 +359,37 @@ def main():
                 "traffic": None if traffic is None else int(traffic["traffic_bytes_per_launch"]),
                 "kernel": KERNEL_NAMES[family], "kernel_avg_ms": round(kern_avg_ms, 4),
                 "algorithmic_bytes_per_launch": int(bm["partial_kernel"])}
+    prefill = T > 16   # a prefill chunk: compute-bound, measured in flops
+    if prefill:
+        flops = flop_model(wl, lens, T)
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        achieved = flops / (kern_avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": KERNEL_NAMES[family], "kernel_avg_ms": round(kern_avg_ms, 4),
+                    "algorithmic_flops_per_launch": int(flops)}
     append = time_append(wl, sh, inp, k_cache, v_cache, dev, 200, step)
     cpu = None
     if not args.no_cpu_baseline and T == 1:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, inp, bounds_np, args.cpu_seconds)
     q = np.percentile(per_step, [10, 50, 90])
+    if prefill:
+        metric, unit = (f"sharded chunked-prefill attention algorithmic TFLOP/s ({T}-token causal "
+                        "chunk against the sharded cache)"), "TFLOP/s"
+    elif wl.kind == "mla":
+        metric, unit = ("sharded decode-attn achieved HBM TB/s (% peak) + decode steps/s, MLA 67K "
+                        "ctx"), "TB/s"
+    else:
+        metric, unit = "sharded decode-attn achieved HBM TB/s (% peak) + decode steps/s", "TB/s"
     line = {
-        "metric": "sharded decode-attn achieved HBM TB/s (% peak) + decode steps/s, MLA 67K ctx"
-        if wl.kind == "mla" else "sharded decode-attn achieved HBM TB/s (% peak) + decode steps/s",
-        "value": round(value, 4), "unit": "TB/s", "n_gpus": 1, "steps": K,
+        "metric": metric,
+        "value": round(value, 4), "unit": unit, "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "steps_per_s": round(1e3 / ms_per_step, 2),
-        "pct_of_hbm_peak": round(100 * value * 1e3 / HBM_PEAK_GBS, 2),
+        "pct_of_hbm_peak": None if prefill else round(100 * value * 1e3 / HBM_PEAK_GBS, 2),
         "ms_per_step_p10_p50_p90": [round(float(x), 4) for x in q],
         "config": {"workload": wl.name if T == 1 else f"{wl.name}-q{T}", "kind": wl.kind,
                    "batch": wl.batch, "query_tokens": T,

@@ -180,16 +180,19 @@ dcp_status dcp_decode_attn(const dcp_attn_shape* shape, const void* q, const voi
                            void* stream);
 
 /*
- * Several query tokens per request (speculative decoding / MTP verification). Both pages name
- * speculative decoding and MTP as what DCP is to be combined with (Qiita article, section
- * on how to view it in practice; naphjohn blog, section 5). A step then scores the q_len
- * newest tokens of each request at once: query token j of request b sits at context position
+ * Several query tokens per request: speculative decoding / MTP verification (2 .. 16 tokens)
+ * and chunked or cached prefill (a chunk of up to 4096 tokens). Both pages name speculative
+ * decoding and MTP as what DCP is to be combined with (Qiita article, section on how to view
+ * it in practice; naphjohn blog, section 5), and the blog's section 4 has DCP reach chunked
+ * prefill (long inputs prefilled chunk by chunk) and cached prefill (reusing KV already
+ * computed). A call scores the q_len newest tokens of each request at once, against the
+ * sharded cache that already holds their K/V: query token j of request b sits at position
  * L_b - q_len + j, where L_b is the largest end among b's ranges in `bounds`, its K/V is
  * already in the cache, and it sees the positions up to and including its own (causal
  * order). The shards, the partials and the merge are as for one token; a row that sees
  * nothing in a shard gets O_s = 0, LSE_s = -inf, and one that sees nothing at all (L_b <
  * q_len - j) gets O = 0, LSE = -inf. q_len = 1 is exactly dcp_decode_attn[_partial].
- *   q_len:     1 .. 16 query tokens per request.
+ *   q_len:     1 .. 4096 query tokens per request.
  *   q:         device [B][q_len][Hq][Dqk] (dtype).
  *   part_o:    device float [B][S][q_len][Hq][Dv];  part_lse: device float [B][S][q_len][Hq].
  *   out:       device float [B][q_len][Hq][Dv];     out_lse:  device float [B][q_len][Hq] or NULL.
@@ -197,8 +200,10 @@ dcp_status dcp_decode_attn(const dcp_attn_shape* shape, const void* q, const voi
  *   the workspace must hold dcp_workspace_bytes_multi(shape, q_len) bytes. dcp_merge_lse merges
  *   these partials when called with num_heads = q_len * Hq.
  * The KV pages are streamed once per group of query rows that share them: MLA takes up to 128
- * rows (q_len * Hq) in one pass, GQA up to 16 rows (q_len * Hq / Hkv) per KV head. Errors
- * additionally: DCP_ERR_SHAPE for q_len outside [1, 16].
+ * rows (q_len * Hq) in one pass, GQA up to 16 rows (q_len * Hq / Hkv) per KV head; a prefill
+ * chunk therefore streams each shard's pages once per row group, as a flash-attention query
+ * block does. The fused call keeps B * S * q_len * Hq partials in the workspace. Errors
+ * additionally: DCP_ERR_SHAPE for q_len outside [1, 4096].
  */
 dcp_status dcp_workspace_bytes_multi(const dcp_attn_shape* shape, int32_t q_len, size_t* bytes);
 dcp_status dcp_decode_attn_multi_partial(const dcp_attn_shape* shape, int32_t q_len,

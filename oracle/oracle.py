@@ -31,7 +31,10 @@ What it computes, and where each step comes from:
   ranges that cover the request), their KV is already in the cache, and token
   j attends to every position up to and including its own (causal order).
   Each shard's partial is then the softmax over the shard's tokens that the
-  row may see, and the same LSE merge gives the causal attention result.
+  row may see, and the same LSE merge gives the causal attention result. The
+  blog's section 4 also has DCP reach chunked and cached prefill: a chunk of
+  new tokens scored against the sharded cache is the same computation with a
+  larger q_len.
 * KV append (``append_token``). Decode makes one token per step and each
   rank keeps only its own slice of the KV (naphjohn blog, section 4, the
   decode bullet; Qiita token-range section). The new token of a request that

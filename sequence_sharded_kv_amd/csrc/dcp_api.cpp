@@ -93,8 +93,8 @@ dcp_status check_shape(const dcp_attn_shape* sh) {
   return DCP_OK;
 }
 
-// Most query tokens per request that the multi-token entry points take.
-constexpr int32_t kMaxQueryTokens = 16;
+// Most query tokens per request that the multi-token entry points take (a prefill chunk).
+constexpr int32_t kMaxQueryTokens = 4096;
 
 dcp_status make_plan(const dcp_attn_shape* sh, int32_t Tq, dcp::Plan* plan) {
   dcp_status st = check_shape(sh);

@@ -352,7 +352,8 @@ def check_multi_rows_are_prefix_decodes():
     position, for every plan and both cache kinds; q_len = 1 is the one-token path."""
     from workloads import workload, make_host_inputs
     rng = np.random.default_rng(21)
-    for name, lens, S, T in (("gqa-tiny", [40, 5], 3, 3), ("gqa-tiny", [17, 2], 2, 4)):
+    for name, lens, S, T in (("gqa-tiny", [40, 5], 3, 3), ("gqa-tiny", [17, 2], 2, 4),
+                             ("gqa-tiny", [40, 9], 3, 20)):   # a chunk crossing shards
         wl = workload(name).replace(lengths=tuple(lens))
         inp = make_host_inputs(wl, lengths=lens)
         caches = (inp["k_cache"], inp["v_cache"])

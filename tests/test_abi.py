@@ -191,7 +191,8 @@ def test_multi_token_shapes_and_errors():
     one = dcp.dcp_workspace_bytes(sh)
     assert dcp.dcp_workspace_bytes_multi(sh, 1) == one
     assert dcp.dcp_workspace_bytes_multi(sh, 4) > one
-    for bad in (0, 17, -1):
+    assert dcp.dcp_workspace_bytes_multi(sh, 4096) > dcp.dcp_workspace_bytes_multi(sh, 16)
+    for bad in (0, 4097, -1):
         with pytest.raises(dcp.DcpError) as e:
             dcp.dcp_workspace_bytes_multi(sh, bad)
         assert e.value.status == dcp.DCP_ERR_SHAPE

@@ -1,7 +1,8 @@
 """GPU parity of several query tokens per request (causal rows) against the float64 oracle:
 partials, the merge and the fused call, for MLA and both GQA kernels, with row counts that
-fit one unit, that need several row groups and that leave padding rows; requests shorter
-than q_len; and q_len = 1 through the multi-token calls against the one-token calls."""
+fit one unit, that need several row groups and that leave padding rows; prefill chunks of
+33-200 tokens; requests shorter than q_len; and q_len = 1 through the multi-token calls
+against the one-token calls."""
 
 import numpy as np
 import pytest
@@ -37,6 +38,14 @@ CASES = [
     ("gqa-d256-valu-t3", "gqa-g16", [700, 70], 3, dict(batch=2, head_dim_qk=256,
                                                       head_dim_v=256)),
     ("gqa-g16-t5-bs24", "gqa-g16", [500, 49], 5, dict(batch=2, block_size=24)),
+    # prefill chunks: many row groups per shard, chunks that cross shard boundaries, and a
+    # request shorter than its chunk
+    ("mla-64h-chunk64", "mla-64h-b512", [1500, 300], 64, dict(batch=2, num_shards=4)),
+    ("mla-16h-chunk96", "mla-64h-b512", [900, 40], 96, dict(batch=2, num_q_heads=16)),
+    ("mla-128h-chunk33", "mla-128h", [700, 90], 33, dict(batch=2)),
+    ("gqa-g16-chunk48", "gqa-g16", [1000, 120], 48, dict(batch=2)),
+    ("gqa-g8-chunk200-S16", "gqa-long", [5000, 600], 200, dict(batch=2, plants_per_head=0)),
+    ("gqa-f32-valu-chunk40", "gqa-g16", [400, 30], 40, dict(batch=2, dtype="f32")),
 ]
 
 

@@ -76,11 +76,12 @@ def _gqa(name, **kw):
 
 
 def _mla(name, **kw):
-    return Workload(
-        name=name, kind=KIND_MLA, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
-        block_size=64, num_shards=8, dtype="bf16", softmax_scale=1.0 / math.sqrt(192.0),
-        length_law="lognormal", length_median=67000.0, length_sigma=0.6,
-        std_latent=0.5, std_rope=1.0, **kw)
+    base = dict(name=name, kind=KIND_MLA, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
+                block_size=64, num_shards=8, dtype="bf16", softmax_scale=1.0 / math.sqrt(192.0),
+                length_law="lognormal", length_median=67000.0, length_sigma=0.6,
+                std_latent=0.5, std_rope=1.0)
+    base.update(kw)
+    return Workload(**base)
 
 
 WORKLOADS = {
@@ -98,6 +99,14 @@ WORKLOADS = {
     "mla-128h": _mla("mla-128h", batch=64, num_q_heads=128, length_cap=131072, seed_index=3),
     # 4: MLA, 64 heads, 512 sequences, lognormal median 67K (the headline)
     "mla-64h-b512": _mla("mla-64h-b512", batch=512, num_q_heads=64, seed_index=4),
+    # prefill chunks scored against the sharded cache (bench.py --q-len 512): MLA at the
+    # agent workload's 5th / 50th / 95th percentile contexts and beyond, GQA at 32K
+    "mla-prefill": _mla("mla-prefill", batch=4, num_q_heads=64, length_law="fixed",
+                        lengths=(20_000, 67_000, 120_000, 180_000), seed_index=6),
+    "gqa-prefill": _gqa(
+        "gqa-prefill", batch=4, num_q_heads=64, num_kv_heads=8, head_dim_qk=128, head_dim_v=128,
+        block_size=16, num_shards=8, dtype="bf16", softmax_scale=1.0 / math.sqrt(128.0),
+        length_law="fixed", lengths=(32_768, 32_768, 32_768, 32_768), seed_index=7),
     # 5: very long GQA contexts with planted high-score keys
     "gqa-long": _gqa(
         "gqa-long", batch=4, num_q_heads=64, num_kv_heads=8, head_dim_qk=128, head_dim_v=128,
