@@ -39,10 +39,12 @@ KERNEL_SOURCES = {
     "mla": ["k_mla_mfma.hip", "device_common.h", "dcp_internal.h"],
     "mla-wide": ["k_mla_mfma.hip", "device_common.h", "dcp_internal.h"],
     "gqa-mfma": ["k_gqa_mfma.hip", "device_common.h", "dcp_internal.h"],
+    "gqa-chunk": ["k_gqa_chunk.hip", "device_common.h", "dcp_internal.h"],
     "gqa-valu": ["k_gqa_valu.hip", "device_common.h", "dcp_internal.h"],
 }
 KERNEL_NAMES = {"mla": "mla_mfma_kernel", "mla-wide": "mla_wide_kernel",
-                "gqa-mfma": "gqa_mfma_kernel", "gqa-valu": "gqa_valu_kernel"}
+                "gqa-mfma": "gqa_mfma_kernel", "gqa-chunk": "gqa_chunk_kernel",
+                "gqa-valu": "gqa_valu_kernel"}
 
 
 def parse_args():
@@ -75,6 +77,8 @@ def kernel_family(wl, q_len=1):
         rows = q_len * wl.num_q_heads
         return "mla-wide" if rows > 64 and wl.num_q_heads % 32 == 0 else "mla"
     g = wl.num_q_heads // wl.num_kv_heads
+    if wl.dtype == "bf16" and g <= 16 and wl.head_dim_qk == 128 and g * q_len > 16:
+        return "gqa-chunk"   # more than 16 query rows per KV head share each K/V tile
     if wl.dtype == "bf16" and g <= 16 and wl.head_dim_qk in (64, 128):
         return "gqa-mfma"
     return "gqa-valu"

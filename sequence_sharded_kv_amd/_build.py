@@ -20,6 +20,7 @@ SOURCES = [
     ("k_util.hip", "k_util", []),
     ("k_gqa_valu.hip", "k_gqa_valu", []),
     ("k_gqa_mfma.hip", "k_gqa_mfma", []),
+    ("k_gqa_chunk.hip", "k_gqa_chunk", []),
     ("k_mla_mfma.hip", "k_mla_mfma", []),
 ]
 

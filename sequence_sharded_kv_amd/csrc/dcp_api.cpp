@@ -56,6 +56,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Upper bounds on workers (stream-K ranges) per kernel family; the launch uses at most this.
 constexpr int32_t kMaxWorkersWave = 4096;  // GQA kernels: one wave per worker
 constexpr int32_t kMaxWorkersMla = 512;    // MLA kernel: one workgroup per worker
+constexpr int32_t kMaxWorkersChunk = 1024; // GQA chunk kernel: one workgroup per worker
 
 dcp_status check_shape(const dcp_attn_shape* sh) {
   if (!sh) return fail(DCP_ERR_NULL, "shape is NULL");
@@ -108,12 +109,20 @@ dcp_status make_plan(const dcp_attn_shape* sh, int32_t Tq, dcp::Plan* plan) {
   const int32_t rows = G * Tq;  // rows that read one KV head
   if (sh->kv_kind == DCP_KV_GQA) {
     const int32_t D = sh->head_dim_qk;
-    if (sh->dtype == DCP_BF16 && G <= 16 && (D == 64 || D == 128))
-      k = Kernel::kGqaMfma;
-    else if (G <= 16 && D % 64 == 0 && D <= 256)
-      k = Kernel::kGqaValu;
-    ru = rows < 16 ? rows : 16;  // one 16-column MFMA block (or 16 VALU rows) per unit
-    pmax = kMaxWorkersWave;
+    if (sh->dtype == DCP_BF16 && G <= 16 && D == 128 && rows > 16) {
+      // several query tokens or a chunk: 32 to 128 rows share each K/V tile
+      k = Kernel::kGqaChunk;
+      ru = 32;
+      while (ru < rows && ru < 128) ru *= 2;
+      pmax = kMaxWorkersChunk;
+    } else {
+      if (sh->dtype == DCP_BF16 && G <= 16 && (D == 64 || D == 128))
+        k = Kernel::kGqaMfma;
+      else if (G <= 16 && D % 64 == 0 && D <= 256)
+        k = Kernel::kGqaValu;
+      ru = rows < 16 ? rows : 16;  // one 16-column MFMA block (or 16 VALU rows) per unit
+      pmax = kMaxWorkersWave;
+    }
   } else {
     if (sh->dtype == DCP_BF16 && sh->head_dim_qk == 576 && sh->head_dim_v == 512 &&
         (sh->num_q_heads == 16 || sh->num_q_heads == 32 || sh->num_q_heads == 64 ||
@@ -227,6 +236,7 @@ dcp_status run_partials(const dcp_attn_shape* sh, int32_t Tq, const void* q, con
   switch (plan.kernel) {
     case dcp::Kernel::kGqaMfma: a.P = dcp::gqa_mfma_workers(dev, a.Dqk, plan.max_workers); break;
     case dcp::Kernel::kGqaValu: a.P = dcp::gqa_valu_workers(dev, plan.max_workers); break;
+    case dcp::Kernel::kGqaChunk: a.P = dcp::gqa_chunk_workers(dev, a.Ru, plan.max_workers); break;
     case dcp::Kernel::kMlaMfma: a.P = dcp::mla_mfma_workers(dev, a.Ru, plan.max_workers); break;
     default: return fail(DCP_ERR_UNSUPPORTED, "no kernel");
   }
@@ -245,6 +255,7 @@ dcp_status run_partials(const dcp_attn_shape* sh, int32_t Tq, const void* q, con
   switch (plan.kernel) {
     case dcp::Kernel::kGqaMfma: e = dcp::launch_gqa_mfma(a, s); break;
     case dcp::Kernel::kGqaValu: e = dcp::launch_gqa_valu(a, sh->dtype, s); break;
+    case dcp::Kernel::kGqaChunk: e = dcp::launch_gqa_chunk(a, s); break;
     case dcp::Kernel::kMlaMfma: e = dcp::launch_mla_mfma(a, s); break;
     default: break;
   }

@@ -52,7 +52,7 @@ struct WsLayout {
   size_t flags, pre, fin, ubounds, qend, redo, piece_o, piece_lse, part_o, part_lse, total;
 };
 
-enum class Kernel { kNone = 0, kGqaValu, kGqaMfma, kMlaMfma };
+enum class Kernel { kNone = 0, kGqaValu, kGqaMfma, kGqaChunk, kMlaMfma };
 
 struct Plan {          // host-side decisions for one shape
   Kernel kernel;
@@ -119,6 +119,8 @@ int32_t gqa_valu_workers(int device, int32_t max_workers);
 hipError_t launch_gqa_valu(const AttnArgs& a, int32_t dtype, hipStream_t stream);
 int32_t gqa_mfma_workers(int device, int32_t Dqk, int32_t max_workers);
 hipError_t launch_gqa_mfma(const AttnArgs& a, hipStream_t stream);
+int32_t gqa_chunk_workers(int device, int32_t Ru, int32_t max_workers);
+hipError_t launch_gqa_chunk(const AttnArgs& a, hipStream_t stream);
 int32_t mla_mfma_workers(int device, int32_t Ru, int32_t max_workers);
 hipError_t launch_mla_mfma(const AttnArgs& a, hipStream_t stream);
 

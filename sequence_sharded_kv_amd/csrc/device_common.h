@@ -48,6 +48,38 @@ __device__ __forceinline__ int32_t piece_slot(int32_t w, bool first_segment) {
   return 2 * w + (first_segment ? 0 : 1);
 }
 
+// ------------------------------------------------------------------ LDS copies
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+  uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Queue one 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane i's 16 bytes
+// land at LDS byte address lds_addr + 16 i. Written as inline asm so that the compiler does
+// not treat every later LDS read as possibly overwritten by it (it would otherwise wait for
+// the next tile's copies before the first transposed read of the current tile); completion
+// is awaited explicitly with vmcnt(0) before the barrier that publishes a tile. M0 is saved
+// and restored.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);  // wave-uniform by contract
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(m0v)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
 // ------------------------------------------------------------------ numerics
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {

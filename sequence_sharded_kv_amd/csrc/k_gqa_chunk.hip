@@ -1,0 +1,343 @@
+// GQA partial attention for units of 32 to 128 query rows per KV head (several query tokens
+// per request, or a prefill chunk), bf16, head_dim 128.
+//
+// The 16-row GQA kernel streams a shard's K/V once per 16 rows. Here a workgroup of NW waves
+// owns 32 * NW rows of one KV head and the waves share each K/V tile through a three-slot LDS
+// ring filled two tiles ahead, so the shard's pages are read once per 32 * NW rows. Per
+// 32-token tile, wave w (rows 32 w .. 32 w + 31):
+//   S[32 tok x 32 rows] = K[32 x 128] . Q^T[128 x 32]   8 x v_mfma_f32_32x32x16_bf16, K rows
+//                                                       from LDS, the rows' Q in registers;
+//   online softmax per row (a lane holds 16 scores of its row, the other 16 are in lane
+//   l ^ 32), each row masked at its own causal limit;
+//   O^T[128 x 32] += V^T[128 x 32 tok] . P[32 tok x 32 rows]   4 M blocks x 2 k steps, V read
+//                                                       transposed from LDS, P as a bf16 high
+//                                                       part and remainder (two MFMAs).
+// The accumulator is 64 registers, so the running max is moved (and O rescaled) whenever it
+// grows, and two waves share each SIMD.
+//
+// Tile layout: per slot a K tile then a V tile, each 32 rows x 256 B; 16-byte chunk c of row r
+// sits at position c ^ sw(r), sw(r) = ((r & 3) << 2) | ((r >> 2) & 3). A 256-byte row spans all
+// 64 banks once, so a chunk's banks depend on its position only; the swizzle spreads the K
+// reads (32 rows, one chunk each) and the transposed V reads over distinct banks. One copy
+// instruction fills 4 rows (lane i: row 4k + i / 16, position i % 16, fetching chunk
+// (i % 16) ^ sw(row)).
+#include "device_common.h"
+
+namespace dcp {
+
+namespace gchunk {
+constexpr int kD = 128;
+constexpr int kRowB = kD * 2;           // 256 bytes per token row
+constexpr int kTileB = 32 * kRowB;      // 8 KB: one K or V tile
+constexpr int kSlotB = 2 * kTileB;      // K tile then V tile
+constexpr int kSlots = 3;
+__device__ __forceinline__ int sw(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+__device__ __forceinline__ bf16x8 tr_pair(const char* lo, const char* hi) {
+  i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)lo);
+  i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)hi);
+  typedef __attribute__((ext_vector_type(8))) short i16x8;
+  i16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return __builtin_bit_cast(bf16x8, z);
+}
+}  // namespace gchunk
+
+template <int NW>  // waves per workgroup, 32 rows each
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gqa_chunk_kernel(AttnArgs a) {
+  using namespace gchunk;
+  constexpr int kDma = 16 / NW;  // copies per wave per tile (8 K + 8 V instructions)
+  __shared__ __attribute__((aligned(1024))) char lds[kSlots * kSlotB];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5;      // lane half: k slice of the 32x32x16 operand layouts
+  const int c32 = lane & 31;    // operand row / column index
+  const int32_t w = blockIdx.x;
+  if (w >= a.P) return;
+  const uint16_t* __restrict__ Q = (const uint16_t*)a.q;
+  const char* __restrict__ Kc = (const char*)a.k;
+  const char* __restrict__ Vc = (const char*)a.v;
+  const int64_t T_pages = a.pre[a.U];
+  const int64_t g0 = worker_begin(T_pages, a.P, w), g1 = worker_begin(T_pages, a.P, w + 1);
+  if (g0 >= g1) return;
+  int32_t u = find_unit(a.pre, a.U, g0);
+  int64_t gg = g0;
+  int32_t bad = 0;
+  const bool bs_pow2 = (a.bs & (a.bs - 1)) == 0;
+  const int bs_shift = __builtin_ctz((unsigned)a.bs);
+  const uint32_t lds0 = lds_u32(&lds[0]);
+
+  // transposed value reads: 16-lane group q4, lane L reads rows 16 kk + 4 (q4 >> 1) + (L >> 2)
+  // and + 8, chunk 4 mt + 2 (q4 & 1) + ((L & 3) >> 1), byte 8 (L & 1) of the chunk
+  const int q4 = lane >> 4, L = lane & 15;
+  const int vr = 4 * (q4 >> 1) + (L >> 2);
+  const int vc = 2 * (q4 & 1) + ((L & 3) >> 1);
+  const int vw = 8 * (L & 1);
+
+  while (gg < g1) {
+    while ((int64_t)a.pre[u + 1] <= gg) ++u;
+    const int64_t up0 = a.pre[u], up1 = a.pre[u + 1];
+    const int64_t sg1 = up1 < g1 ? up1 : g1;
+    const int32_t per_bs = a.Hkv * a.NRg;
+    const int32_t bsi = u / per_bs, hsub = u - bsi * per_bs;
+    const int32_t kvh = hsub / a.NRg, rg = hsub - kvh * a.NRg;
+    const int32_t b = bsi / a.S;
+    const int64_t ta = a.ubounds[2 * bsi], te = a.ubounds[2 * bsi + 1];
+    const int64_t pa = ta / a.bs;
+    int64_t t0 = (pa + (gg - up0)) * a.bs, t1 = (pa + (sg1 - up0)) * a.bs;
+    if (t0 < ta) t0 = ta;
+    if (t1 > te) t1 = te;
+    const bool whole = (gg == up0) && (sg1 == up1);
+    const bool first = (gg == g0);
+    const int32_t* brow = a.block_table + (int64_t)b * a.max_blocks;
+    const int32_t t0i = (int32_t)t0, t1i = (int32_t)t1;
+    const int32_t ntiles = (t1i - t0i + 31) / 32;  // >= 1
+    auto page_idx = [&](int32_t t) -> int32_t { return bs_pow2 ? (t >> bs_shift) : t / a.bs; };
+    const int32_t plast_seg = page_idx(t1i - 1);
+
+    // this lane's query row (MFMA column c32 of the wave's 32 rows) and its causal limit
+    int32_t jq = 0;
+    const int32_t rho = unit_row(a, kvh, rg, 32 * wv + c32, &jq);
+    const bool row_ok = rho >= 0;
+    const int32_t lim = (a.Tq == 1 || !row_ok) ? INT32_MAX : a.qend[b] + jq;
+
+    // Block ids of the segment's pages, 64 at a time: lane j holds the id of page pchunk + j.
+    int32_t pchunk = -1, pid = -1;
+    auto ensure_pages = [&](int32_t pfirst, int32_t plast) {
+      if (pchunk < 0 || plast >= pchunk + 64) {
+        pchunk = pfirst;
+        const int32_t pp = pchunk + lane;
+        pid = (pp <= plast_seg) ? brow[pp] : -1;
+        asm volatile("" : "+v"(pid));  // keep the wait for this load inside the branch
+      }
+    };
+
+    // Queue tile i into slot i % kSlots: this wave's copy instructions k = wv + NW m of the K
+    // tile and of the V tile. Lane t < 32 first forms the byte offset of token tile + t's row
+    // (or marks it invalid); returns the tile's valid-token mask.
+    auto issue_tile = [&](int32_t i) -> uint32_t {
+      const int32_t tile = t0i + 32 * i;
+      const int32_t tl = (tile + 31 < t1i ? tile + 31 : t1i - 1);
+      const int32_t pfirst = page_idx(tile), plast = page_idx(tl);
+      ensure_pages(pfirst, plast);
+      const int32_t t = tile + c32;
+      const int32_t tc = t < t1i ? t : t1i - 1;
+      const int32_t mypage = page_idx(tc);
+      int32_t blk = -1;
+      for (int32_t pg = pfirst; pg <= plast; ++pg) {
+        const int32_t id = __builtin_amdgcn_readlane(pid, pg - pchunk);
+        blk = (mypage == pg) ? id : blk;
+      }
+      const bool page_ok = blk >= 0 && blk < a.num_blocks;
+      const uint32_t slot = bs_pow2 ? (uint32_t)(tc & (a.bs - 1)) : (uint32_t)(tc % a.bs);
+      const uint32_t row = ((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)kvh) * (uint32_t)a.bs + slot;
+      // byte offset of the row in the caches; -1 sends the copy to the workspace's zero row
+      const int64_t off = page_ok ? (int64_t)row * kRowB : -1;
+      bad |= __any(lane < 32 && !page_ok) ? 1 : 0;
+      const uint32_t mask = (uint32_t)__ballot(lane < 32 && page_ok && t < t1i);
+      const uint32_t base = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((i % kSlots) * kSlotB));
+      const int sub = lane >> 4, p = lane & 15;
+#pragma unroll
+      for (int m = 0; m < 8 / NW; ++m) {
+        const int k = wv + NW * m;  // rows 4k .. 4k + 3
+        int64_t ro = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int32_t lo = __builtin_amdgcn_readlane((uint32_t)off, 4 * k + e);
+          const int32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)off >> 32), 4 * k + e);
+          const int64_t oe = (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+          ro = (sub == e) ? oe : ro;
+        }
+        const int r = 4 * k + sub;
+        const int64_t chunk = 16 * (p ^ sw(r));
+        const char* ks = ro >= 0 ? Kc + ro + chunk : a.zero_row + chunk;
+        const char* vs = ro >= 0 ? Vc + ro + chunk : a.zero_row + chunk;
+        dma16(ks, base + k * 1024);
+        dma16(vs, base + kTileB + k * 1024);
+      }
+      return mask;
+    };
+    auto wait_tiles = [&](int32_t later) {  // at most `later` tiles' copies in flight
+      if (later >= 1)
+        __builtin_amdgcn_s_waitcnt((kDma & 15) | ((kDma >> 4) << 14) | (7 << 4) | (15 << 8));
+      else
+        __builtin_amdgcn_s_waitcnt(0);
+    };
+
+    // Q^T as the B operand: lane holds q[row][16 ks + 8 g .. +8]
+    bf16x8 qop[8];
+    {
+      const uint16_t* qrow = Q + ((int64_t)b * a.R + (row_ok ? rho : 0)) * kD + 8 * g;
+      u32x4 raw[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) raw[ks] = *(const u32x4*)(qrow + 16 * ks);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        asm volatile("" : "+v"(raw[ks]));  // resident: no reload inside the tile loop
+        qop[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
+      }
+    }
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
+    float m_run = kNegInf, l_run = 0.f;
+
+    uint32_t maskv = 0;  // lane s: valid-token mask of the tile in slot s
+    int32_t issued = 0;
+    for (int k = 0; k < kSlots - 1; ++k)
+      if (issued < ntiles) {
+        const uint32_t m = issue_tile(issued);
+        maskv = (lane == issued % kSlots) ? m : maskv;
+        ++issued;
+      }
+    wait_tiles(issued - 1);
+    __syncthreads();
+
+    for (int32_t i = 0; i < ntiles; ++i) {
+      if (issued < ntiles) {
+        const uint32_t m = issue_tile(issued);
+        maskv = (lane == issued % kSlots) ? m : maskv;
+        ++issued;
+      }
+      const int32_t tile = t0i + 32 * i;
+      const char* tk = &lds[(i % kSlots) * kSlotB];
+      const char* tv = tk + kTileB;
+      const int32_t dl = lim - tile;
+      const uint32_t mask = __builtin_amdgcn_readlane(maskv, i % kSlots) &
+                            (dl < 0 ? 0u : dl >= 31 ? 0xFFFFFFFFu : (2u << dl) - 1u);
+
+      // S[32 tok x 32 rows] = K . Q^T
+      int fq = sw(c32);
+      asm volatile("" : "+v"(fq));
+      const char* krow = tk + c32 * kRowB;
+      f32x16 st;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[r] = 0.f;
+      bf16x8 kbuf[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kbuf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(krow + 16 * ((2 * ks + g) ^ fq)));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 kop = kbuf[ks & 3];
+        if (ks + 4 < 8)
+          kbuf[ks & 3] = __builtin_bit_cast(
+              bf16x8, *(const u32x4*)(krow + 16 * ((2 * (ks + 4) + g) ^ fq)));
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], st, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // online softmax of row c32; st[r] is token 8 (r / 4) + 4 g + r % 4
+      float x[16];
+      float tmax = kNegInf;
+      const uint32_t hmask = mask >> (4 * g);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        x[r] = ((hmask >> (8 * (r >> 2) + (r & 3))) & 1u) ? st[r] * a.scale_log2 : kNegInf;
+        tmax = fmaxf(tmax, x[r]);
+      }
+      {
+        auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
+                                                   false, false);
+        tmax = fmaxf(__uint_as_float(s2[0]), __uint_as_float(s2[1]));
+      }
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+      if (!__all(alpha == 1.f)) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt] *= alpha;
+      }
+      float psum = 0.f;
+      bf16x8 phi[2], plo[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = (x[r] == kNegInf) ? 0.f : fast_exp2(x[r] - m_new);
+        psum += pv;
+        const __bf16 hi = (__bf16)pv;
+        phi[r >> 3][r & 7] = hi;
+        plo[r >> 3][r & 7] = (__bf16)(pv - (float)hi);
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+
+      // O^T[128 x 32 rows] += V^T . P over two 16-token k steps
+      int vcq = vc;
+      asm volatile("" : "+v"(vcq));
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) {
+        const int kk = s2 >> 2, mt = s2 & 3;
+        const int r1 = 16 * kk + vr;
+        const bf16x8 vop =
+            tr_pair(tv + r1 * kRowB + vw + 16 * ((vcq + 4 * mt) ^ sw(r1)),
+                    tv + (r1 + 8) * kRowB + vw + 16 * ((vcq + 4 * mt) ^ sw(r1 + 8)));
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, phi[kk], acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, plo[kk], acc[mt], 0, 0, 0);
+      }
+      // tile i + 1 has landed and every wave is past tile i (its slot is refilled next)
+      wait_tiles(issued - (i + 2));
+      __syncthreads();
+    }
+
+    // finalise: l over the two lanes of row c32
+    float l = l_run;
+    {
+      auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false,
+                                                 false);
+      l = __uint_as_float(s2[0]) + __uint_as_float(s2[1]);
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float* dst_o;
+    float* dst_l;
+    if (whole) {
+      dst_o = a.part_o + ((int64_t)bsi * a.R + rho) * kD;
+      dst_l = a.part_lse + (int64_t)bsi * a.R + rho;
+    } else {
+      const int32_t slot = piece_slot(w, first);
+      dst_o = a.piece_o + ((int64_t)slot * a.Ru + 32 * wv + c32) * kD;
+      dst_l = a.piece_lse + (int64_t)slot * a.Ru + 32 * wv + c32;
+    }
+    if (row_ok) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(f32x4*)(dst_o + 32 * mt + 8 * r4 + 4 * g) =
+              f32x4{acc[mt][4 * r4], acc[mt][4 * r4 + 1], acc[mt][4 * r4 + 2],
+                    acc[mt][4 * r4 + 3]} * inv;
+      if (g == 0) *dst_l = l > 0.f ? (m_run + fast_log2(l)) * kLn2 : kNegInf;
+    }
+    gg = sg1;
+  }
+  if (bad && lane == 0) atomicOr(a.flags, kFlagBadBlock);
+}
+
+int32_t gqa_chunk_workers(int device, int32_t Ru, int32_t max_workers) {
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  // two waves per SIMD (8 per CU) by registers; 48 KB of LDS per workgroup
+  const int nw = Ru / 32;
+  const int by_regs = 8 / nw, by_lds = 160 / 48;
+  const int per_cu = by_regs < by_lds ? by_regs : by_lds;
+  int32_t p = cus * per_cu;
+  return p < max_workers ? p : max_workers;
+}
+
+hipError_t launch_gqa_chunk(const AttnArgs& a, hipStream_t stream) {
+  switch (a.Ru / 32) {
+    case 1: hipLaunchKernelGGL((gqa_chunk_kernel<1>), dim3(a.P), dim3(64), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((gqa_chunk_kernel<2>), dim3(a.P), dim3(128), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((gqa_chunk_kernel<4>), dim3(a.P), dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dcp

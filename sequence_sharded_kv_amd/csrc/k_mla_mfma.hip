@@ -64,36 +64,6 @@ __device__ __forceinline__ float quad_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
-  uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
-  uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Queue one 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane i's 16 bytes
-// land at LDS byte address lds_addr + 16 i. Written as inline asm so that the compiler does
-// not treat every later LDS read as possibly overwritten by it (it would otherwise wait for
-// the next tile's copies before the first transposed read of the current tile); completion
-// is awaited explicitly with vmcnt(0) before the barrier that publishes a tile. M0 is saved
-// and restored.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);  // wave-uniform by contract
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(gptr), "s"(m0v)
-      : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
-}
-
 template <int NW>  // waves per workgroup; 16 heads per wave, Hq = 16 * NW
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row, const int32_t* __restrict__ only) {
