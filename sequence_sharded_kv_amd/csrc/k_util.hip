@@ -222,6 +222,7 @@ hipError_t launch_finish_units(const AttnArgs& a, hipStream_t stream) {
 
 // out[b, h, :] = sum_s exp(LSE_s - LSE) O_s with LSE = M + ln sum_s exp(LSE_s - M).
 // One thread per 4 output values; a workgroup covers 256 x 4 values of one or more heads.
+constexpr int32_t kMergeUnroll = 16;  // shard counts up to this keep every load in flight
 __global__ void __launch_bounds__(256)
 merge_kernel(int32_t B, int32_t S, int32_t H, int32_t Dv, const float* __restrict__ part_o,
              const float* __restrict__ part_lse, float* __restrict__ out,
@@ -233,17 +234,36 @@ merge_kernel(int32_t B, int32_t S, int32_t H, int32_t Dv, const float* __restric
   const int32_t c = (int32_t)(q4 % dv4);
   const int64_t b = bh / H, h = bh % H;
   const float* lse = part_lse + b * S * H + h;
+  const float* po = part_o + (b * S * H + h) * Dv + 4 * c;
+  const int64_t so = (int64_t)H * Dv;  // stride between shards
   float m = kNegInf;
-  for (int32_t s = 0; s < S; ++s) m = fmaxf(m, lse[(int64_t)s * H]);
   float den = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int32_t s = 0; s < S; ++s) {
-    // Loads are unconditional so that all S of them are in flight together; a shard with
-    // zero weight (LSE = -inf) contributes nothing whatever its O holds.
-    const float w = safe_exp_diff(lse[(int64_t)s * H], m);
-    const f32x4 o = *(const f32x4*)(part_o + ((b * S + s) * H + h) * Dv + 4 * c);
+  // A shard with zero weight (LSE = -inf) contributes nothing whatever its O holds.
+  auto add = [&](float l, const f32x4& o) {
+    const float w = safe_exp_diff(l, m);
     den += w;
     if (w != 0.f) acc += w * o;
+  };
+  if (S <= kMergeUnroll) {
+    // all 2 S loads queued before the first use
+    float l[kMergeUnroll];
+    f32x4 o[kMergeUnroll];
+#pragma unroll
+    for (int32_t s = 0; s < kMergeUnroll; ++s)
+      if (s < S) {
+        l[s] = lse[(int64_t)s * H];
+        o[s] = *(const f32x4*)(po + s * so);
+      }
+#pragma unroll
+    for (int32_t s = 0; s < kMergeUnroll; ++s)
+      if (s < S) m = fmaxf(m, l[s]);
+#pragma unroll
+    for (int32_t s = 0; s < kMergeUnroll; ++s)
+      if (s < S) add(l[s], o[s]);
+  } else {
+    for (int32_t s = 0; s < S; ++s) m = fmaxf(m, lse[(int64_t)s * H]);
+    for (int32_t s = 0; s < S; ++s) add(lse[(int64_t)s * H], *(const f32x4*)(po + s * so));
   }
   float inv = den > 0.f ? 1.f / den : 0.f;
   *(f32x4*)(out + bh * Dv + 4 * c) = acc * inv;

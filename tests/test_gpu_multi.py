@@ -157,3 +157,48 @@ def test_wide_mla_recomputes_workers_whose_scores_outrun_the_first_tile():
                               wl.head_dim_v)
     assert float(np.max(fl[0])) > 80.0
     assert_close(out.cpu().numpy(), out_lse.cpu().numpy(), fo, fl, wl.dtype, "planted wide")
+
+
+@pytest.mark.parametrize("wl_name,over,lengths,T", [
+    ("gqa-g16", dict(batch=2), [300, 200], 4),       # 64 rows per KV head: gqa_chunk_kernel
+    ("mla-64h-b512", dict(batch=2), [300, 200], 2),  # 128 rows: mla_wide_kernel
+    ("mla-128h", dict(batch=2), [300, 200], 1),      # 128 heads: mla_wide_kernel
+])
+def test_multi_row_kernels_flag_invalid_device_values(wl_name, over, lengths, T):
+    """The kernels for many rows per KV tile mask a block id outside the pool and clamp a
+    bound past the table like the others: flags set, other requests exact, output finite."""
+    say(f"[gpu] device-side validation, {wl_name} q_len {T}")
+    wl = workload(wl_name).replace(**over)
+    host = make_host_inputs(wl, lengths=lengths)
+    inp = to_device(wl, host)
+    qh = make_queries(wl, T)
+    q = _q_device(wl, qh)
+    sh = shape_of(wl, inp)
+    B, S, Hq, Dv = wl.batch, wl.num_shards, wl.num_q_heads, wl.head_dim_v
+    k = inp["kv_cache"] if wl.kind == "mla" else inp["k_cache"]
+    v = None if wl.kind == "mla" else inp["v_cache"]
+    bounds_np = dcp.dcp_plan_shards(host["seq_lens"], S, wl.block_size)
+    ws = dcp.alloc_workspace(sh, "cuda", T)
+    out = torch.empty((B, T, Hq, Dv), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device="cuda")
+    bt = inp["block_table"].clone()
+    bt[1, 0] = int(host["num_blocks"]) + 7
+    dcp.dcp_decode_attn_multi(sh, T, q, k, v, bt, torch.from_numpy(bounds_np).cuda(), ws, out, lse)
+    torch.cuda.synchronize()
+    assert dcp.dcp_read_device_flags(ws) & 2
+    assert torch.isfinite(out).all()
+    _, caches, hbt, _ = host_inputs_of(wl, inp)
+    ro, rl = O.partial_attention_multi(wl.kind, wl.dtype, qh, caches, hbt,
+                                       np.asarray(bounds_np, np.int64), wl.block_size,
+                                       wl.softmax_scale, Dv, seqs=[0])
+    fo, fl = O.merge_lse(ro[:1].reshape(1, S, T * Hq, Dv), rl[:1].reshape(1, S, T * Hq))
+    assert_close(out.cpu().numpy()[:1].reshape(1, T * Hq, Dv),
+                 lse.cpu().numpy()[:1].reshape(1, T * Hq), fo, fl, wl.dtype,
+                 f"{wl_name} untouched request")
+    big = bounds_np.copy()
+    big[0, -1, 1] = 10 ** 9
+    dcp.dcp_decode_attn_multi(sh, T, q, k, v, inp["block_table"], torch.from_numpy(big).cuda(), ws,
+                              out, lse)
+    torch.cuda.synchronize()
+    assert dcp.dcp_read_device_flags(ws) & 1
+    assert torch.isfinite(out).all()
