@@ -66,6 +66,9 @@ def parse_args():
                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                         "script and print the traffic JSON")
     p.add_argument("--pmc-calibration-gib", type=float, default=1.0)
+    p.add_argument("--summarize-mfma", metavar="MFMA_DIR",
+                   help="summarise a rocprofv3 --pmc run (MfmaUtil MfmaFlopsBF16 "
+                        "SQ_INSTS_VALU_MFMA_BF16) of this script and print the MFMA JSON")
     return p.parse_args()
 
 
@@ -129,8 +132,12 @@ def traffic_file(workload):
     return os.path.join(PROFILES, f"traffic_{workload}.json")
 
 
-def load_traffic(workload, family):
-    path = traffic_file(workload)
+def mfma_file(workload):
+    return os.path.join(PROFILES, f"mfma_{workload}.json")
+
+
+def load_traffic(workload, family, path=None):
+    path = path or traffic_file(workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -162,18 +169,41 @@ def summarize_pmc(fetch_dir, write_dir, workload, family, calib_gib):
     ref_bytes = calib_gib * (1 << 30)
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _read_counter_csv(d, name)
-        ker = [v for _, k, v in rows if KERNEL_NAMES[family] in k]
-        ref = [v for _, k, v in rows if "elementwise" in k.lower() and v * 1024 > 0.5 * ref_bytes]
-        if not ker or not ref:
-            raise SystemExit(f"{name}: no dispatches of {KERNEL_NAMES[family]} or of the reference "
-                             f"pass in {d}")
-        scale = ref_bytes / (ref[0] * 1024.0)
+        ker = [(i, v) for i, k, v in rows if KERNEL_NAMES[family] in k]
+        if not ker:
+            raise SystemExit(f"{name}: no dispatches of {KERNEL_NAMES[family]} in {d}")
+        # the reference pass is the last elementwise dispatch before the first attention step
+        # (the input generators before it are elementwise kernels too)
+        ref = [v for i, k, v in rows if "elementwise" in k.lower() and i < ker[0][0]]
+        if not ref or not 0.25 * ref_bytes <= ref[-1] * 1024 <= 4 * ref_bytes:
+            raise SystemExit(f"{name}: no reference pass of about {calib_gib} GiB before the "
+                             f"first {KERNEL_NAMES[family]} dispatch in {d}")
+        ker = [v for _, v in ker]
+        scale = ref_bytes / (ref[-1] * 1024.0)
         out[name.lower() + "_kib_raw_mean"] = float(np.mean(ker))
         out[name.lower() + "_calibration_scale"] = scale
         out[name.lower() + "_bytes_per_launch"] = float(np.mean(ker)) * 1024.0 * scale
         out[name.lower() + "_dispatches"] = len(ker)
     out["traffic_bytes_per_launch"] = out["fetch_size_bytes_per_launch"] + \
         out["write_size_bytes_per_launch"]
+    return out
+
+
+def summarize_mfma(d, workload, family, wl):
+    """MFMA counters of the dominant kernel, averaged over its dispatches: MfmaUtil (percent of
+    the GPU-active cycles during which the SIMDs' matrix units are busy, summed over SIMDs),
+    MfmaFlopsBF16 (bf16 MFMA operations issued, 512 per MOPS count) and the instruction count.
+    Issued flops include the second value product of the split weights and padding rows."""
+    out = {"workload": workload, "kernel": KERNEL_NAMES[family],
+           "kernel_sources_sha256": sources_sha(family)}
+    for name, key in (("MfmaUtil", "mfma_busy_pct"), ("MfmaFlopsBF16", "mfma_flops_per_launch"),
+                      ("SQ_INSTS_VALU_MFMA_BF16", "mfma_instructions_per_launch")):
+        ker = [v for _, k, v in _read_counter_csv(d, name) if KERNEL_NAMES[family] in k]
+        if not ker:
+            raise SystemExit(f"{name}: no dispatches of {KERNEL_NAMES[family]} in {d}")
+        out[key] = float(np.mean(ker))
+        out[key.replace("_per_launch", "") + "_dispatches"] = len(ker)
+    out["flops_per_instruction"] = out["mfma_flops_per_launch"] / out["mfma_instructions_per_launch"]
     return out
 
 
@@ -278,6 +308,10 @@ def main():
         print(json.dumps(summarize_pmc(*args.summarize_pmc, args.workload, family,
                                        args.pmc_calibration_gib), indent=1))
         return 0
+    if args.summarize_mfma:
+        print(json.dumps(summarize_mfma(args.summarize_mfma, args.workload, family, wl),
+                         indent=1))
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: this build runs every shard on one device and issues "
@@ -363,6 +397,18 @@ def main():
                 "traffic": None if traffic is None else int(traffic["traffic_bytes_per_launch"]),
                 "kernel": KERNEL_NAMES[family], "kernel_avg_ms": round(kern_avg_ms, 4),
                 "algorithmic_bytes_per_launch": int(bm["partial_kernel"])}
+    # matrix-unit use of the same kernel, from a committed rocprofv3 --pmc summary taken on
+    # the same kernel sources (null once they have changed)
+    mf = load_traffic(wl.name, family, mfma_file(wl.name)) if T == 1 else None
+    mfma = None
+    if mf is not None:
+        issued = mf["mfma_flops_per_launch"] / (kern_avg_ms * 1e-3) / 1e12
+        algo = flop_model(wl, lens, 1)
+        mfma = {"busy_pct": round(mf["mfma_busy_pct"], 2),
+                "issued_tflops": round(issued, 1), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                "issued_frac": round(issued / MFMA_BF16_PEAK_TFLOPS, 4),
+                "issued_flops_per_launch": int(mf["mfma_flops_per_launch"]),
+                "algorithmic_flops_per_launch": int(algo)}
     prefill = T > 16   # a prefill chunk: compute-bound, measured in flops
     if prefill:
         flops = flop_model(wl, lens, T)
@@ -404,6 +450,7 @@ def main():
                    "kv_bytes": bm["kv"], "algorithmic_bytes_per_step": bm["step"],
                    "parallelism": "all shards on one GPU"},
         "roofline": roofline,
+        "mfma": mfma,
         "cpu_baseline": cpu,
         "append_kv": append,
     }
