@@ -151,8 +151,9 @@ hipError_t launch_schedule(const int32_t* bounds, int32_t B, int32_t S, int32_t 
 // query row of the partials.
 constexpr int kFinishThreads = 256;
 constexpr int kFinishMaxPieces = 4096;  // >= the most workers any launch uses
+constexpr int kFinishUnroll = 4;        // pieces whose loads are issued together
 
-__global__ void __launch_bounds__(kFinishThreads)
+__global__ void __launch_bounds__(kFinishThreads) __attribute__((amdgpu_waves_per_eu(8)))
 finish_units_kernel(AttnArgs a) {
   __shared__ int32_t slots[kFinishMaxPieces];  // -1 for workers that own no pages
   const int32_t count = a.flags[1];
@@ -188,18 +189,37 @@ finish_units_kernel(AttnArgs a) {
     }
     __syncthreads();
     if (rho < 0) continue;
-    float m = kNegInf;
-    for (int32_t k = 0; k < ns; ++k)
-      if (slots[k] >= 0) m = fmaxf(m, a.piece_lse[(int64_t)slots[k] * Hu + h]);
-    float den = 0.f;
+    // One pass over the pieces, kFinishUnroll at a time so that their loads are in flight
+    // together: the running max m moves to the batch's max and the sums so far are rescaled
+    // by exp(m_old - m_new) (the same re-weighting as the LSE merge).
+    float m = kNegInf, den = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int32_t k = 0; k < ns; ++k) {
-      const int32_t sl = slots[k];
-      if (sl < 0) continue;
-      const float wt = safe_exp_diff(a.piece_lse[(int64_t)sl * Hu + h], m);
-      const f32x4 o = ((const f32x4*)(a.piece_o + (int64_t)sl * Hu * a.Dv))[i4];
-      den += wt;
-      acc += wt * o;
+    for (int32_t k0 = 0; k0 < ns; k0 += kFinishUnroll) {
+      float lb[kFinishUnroll];
+      f32x4 ob[kFinishUnroll];
+#pragma unroll
+      for (int j = 0; j < kFinishUnroll; ++j) {
+        const int32_t sl = (k0 + j < ns) ? slots[k0 + j] : -1;
+        lb[j] = kNegInf;
+        ob[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (sl >= 0) {
+          lb[j] = a.piece_lse[(int64_t)sl * Hu + h];
+          ob[j] = ((const f32x4*)(a.piece_o + (int64_t)sl * Hu * a.Dv))[i4];
+        }
+      }
+      float mb = m;
+#pragma unroll
+      for (int j = 0; j < kFinishUnroll; ++j) mb = fmaxf(mb, lb[j]);
+      const float sc = safe_exp_diff(m, mb);  // 0 while both are -inf (nothing summed yet)
+      den *= sc;
+      acc *= sc;
+#pragma unroll
+      for (int j = 0; j < kFinishUnroll; ++j) {
+        const float wt = safe_exp_diff(lb[j], mb);
+        den += wt;
+        acc += wt * ob[j];
+      }
+      m = mb;
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     ((f32x4*)out_o)[c4] = acc * inv;
