@@ -150,6 +150,50 @@ def test_any_partition_merges_to_full_attention(wl_name, over, lengths):
         assert_close(po.cpu().numpy(), pl.cpu().numpy(), ro, rl, wl.dtype, f"{wl_name} S={S} parts")
 
 
+@pytest.mark.parametrize("wl_name,over,lengths", [
+    ("mla-64h-b512", dict(batch=3), [1000, 77, 4097]),                   # 16 rows per wave
+    ("mla-128h", dict(batch=2), [2000, 45]),                            # 32 rows per wave
+    ("mla-64h-b512", dict(batch=2, block_size=16), [500, 77]),         # tiles over 2 pages
+    ("gqa-g16", dict(batch=3), [1000, 77, 3001]),                       # MFMA kernel
+    ("gqa-g16", dict(batch=2, dtype="f32"), [700, 45]),                 # VALU kernel
+], ids=["mla-64h", "mla-128h", "mla-64h-bs16", "gqa-g16", "gqa-g16-f32"])
+def test_unused_slots_past_the_context_stay_out_of_the_output(wl_name, over, lengths):
+    """A page's slots past the context end may hold anything in a real cache. Filled with NaN
+    here, they must not reach the output: masked tokens get weight 0, and 0 * NaN would
+    poison the value product if a kernel copied those slots."""
+    say(f"[gpu] NaN past the context: {wl_name} {over} {lengths}")
+    wl = workload(wl_name).replace(**over)
+    if wl.length_law == "fixed":
+        wl = wl.replace(lengths=tuple(lengths))
+    host = make_host_inputs(wl, lengths=lengths)
+    inp = to_device(wl, host)
+    bt = host["block_table"]
+    names = ("kv_cache",) if wl.kind == "mla" else ("k_cache", "v_cache")
+    filled = 0
+    for b, L in enumerate(lengths):
+        tail = L % wl.block_size
+        if tail == 0:
+            continue
+        page = int(bt[b, L // wl.block_size])
+        for n in names:
+            if wl.kind == "mla":
+                inp[n][page, tail:, :] = float("nan")
+            else:
+                inp[n][page, :, tail:, :] = float("nan")
+        filled += wl.block_size - tail
+    assert filled > 0
+    hin = host_inputs_of(wl, inp)
+    bounds_np = dcp.dcp_plan_shards(host["seq_lens"], wl.num_shards, wl.block_size)
+    bounds = torch.from_numpy(bounds_np).cuda()
+    fo, fl, ws = run_fused(wl, inp, bounds)
+    torch.cuda.synchronize()
+    assert dcp.dcp_read_device_flags(ws) == 0
+    o, l = fo.cpu().numpy(), fl.cpu().numpy()
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    fo_ref, fl_ref = oracle_full(wl, hin)
+    assert_close(o, l, fo_ref, fl_ref, wl.dtype, f"{wl_name} NaN past the context")
+
+
 def test_workspace_reuse_poison_and_determinism():
     say("[gpu] workspace reuse")
     wl = workload("mla-64h-b512").replace(batch=3)
