@@ -125,17 +125,59 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row, const int32_t* __
     // The rows' source addresses are wave-uniform and held in scalar registers in between.
     constexpr int kRows = kMlaTile / NW;
     uint64_t row_src[kRows];
+    uint64_t rbase = 0;      // one-page tiles: source of row 0
+    uint32_t rstride = 0;    // one-page tiles: bytes between rows (0 for the zero row)
+    int32_t rlast = 0;       // one-page tiles: last row before t1 (later rows repeat it)
+    int32_t one = 0;         // wave-uniform: the pending tile lies in one page
     uint32_t base_pend = 0;
     auto issue_rows = [&](int k0, int k1) {
+      if (one) {
 #pragma unroll
-      for (int k = k0; k < k1; ++k)
-        dma16((const char*)row_src[k] + 16 * lane, base_pend + (wv + k * NW) * kMlaRowA);
+        for (int k = k0; k < k1; ++k) {
+          const int r = wv + k * NW;
+          const uint32_t rr = (uint32_t)(r < rlast ? r : rlast);
+          dma16((const char*)(rbase + (uint64_t)(rr * rstride)) + 16 * lane,
+                base_pend + r * kMlaRowA);
+        }
+      } else {
+#pragma unroll
+        for (int k = k0; k < k1; ++k)
+          dma16((const char*)row_src[k] + 16 * lane, base_pend + (wv + k * NW) * kMlaRowA);
+      }
     };
     // Queue the copy of tile [tile, tile + 32) into buffer `buf` (all region-A rows, or the
     // first half of them with the rest left to issue_rows); returns the valid-token mask.
     auto issue_tile = [&](int32_t tile, int buf, bool all) -> uint32_t {
       const int32_t blk = blk_next;
       if (tile + kMlaTile < t1i) blk_next = page_of(tile + kMlaTile);
+      const uint32_t base = lds_u32(&lds[buf][0]);
+      base_pend = base;
+      one = bs_pow2 ? ((tile >> bs_shift) == ((tile + kMlaTile - 1) >> bs_shift))
+                    : (tile / a.bs == (tile + kMlaTile - 1) / a.bs);
+      if (one) {
+        // rows tile .. tile + 31 lie in one page; rows past t1 repeat the last valid row (the
+        // page's later slots may hold anything, and a NaN there would survive its zero weight
+        // in the value product)
+        const int32_t blk1 = __builtin_amdgcn_readfirstlane(blk);
+        const bool page_ok = blk1 >= 0 && blk1 < a.num_blocks;
+        const uint32_t slot0 = bs_pow2 ? (uint32_t)(tile & (a.bs - 1)) : (uint32_t)(tile % a.bs);
+        rbase = page_ok ? (uint64_t)Kc + ((uint64_t)(uint32_t)blk1 * (uint32_t)a.bs + slot0) *
+                                             (kMlaDqk * 2)
+                        : (uint64_t)zero_row;
+        rstride = page_ok ? kMlaDqk * 2 : 0;
+        rlast = t1i - 1 - tile;
+        if (!page_ok) bad = 1;
+        const uint32_t m = (uint32_t)__ballot(page_ok && lane < kMlaTile && tile + lane < t1i);
+        issue_rows(0, all ? kRows : kRows / 2);
+        for (int kk = wv; kk < 4; kk += NW) {
+          const int r = 8 * kk + (lane >> 3);
+          const uint32_t rr = (uint32_t)(r < rlast ? r : rlast);
+          const uint64_t ra = rbase + (uint64_t)(rr * rstride);
+          dma16((const char*)ra + 1024 + 16 * ((lane & 7) ^ swz_b(r)),
+                base + kMlaRegionB + kk * 1024);
+        }
+        return m;
+      }
       uint64_t rowaddr = (uint64_t)zero_row;
       bool valid = false;
       if (lane < kMlaTile) {
@@ -153,10 +195,8 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row, const int32_t* __
         valid = page_ok && t < t1i;
       }
       const uint32_t mask = (uint32_t)__ballot(valid);
-      const uint32_t base = lds_u32(&lds[buf][0]);
 #pragma unroll
       for (int k = 0; k < kRows; ++k) row_src[k] = readlane_u64(rowaddr, wv + k * NW);
-      base_pend = base;
       issue_rows(0, all ? kRows : kRows / 2);
       for (int kk = wv; kk < 4; kk += NW) {
         // lane covers row 8 kk + lane / 8: pick its address among the eight rows' addresses
