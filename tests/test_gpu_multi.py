@@ -122,14 +122,16 @@ def test_multi_with_one_token_equals_one_token_calls(wl_name, over, lengths):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_wide_mla_recomputes_workers_whose_scores_outrun_the_first_tile():
-    """128 query rows per unit take the 32-rows-per-wave kernel, whose weights are relative
-    to each segment's first-tile maximum. Two keys planted mid-shard score about 90 (natural
-    log units) above the rest, so those workers are recomputed by the general kernel: the
-    result still matches the oracle and flag bit 2 reports the recomputation."""
+@pytest.mark.parametrize("wl_name", ["mla-128h", "mla-64h-b512"])
+def test_lazy_max_mla_recomputes_workers_whose_scores_outrun_the_first_tile(wl_name):
+    """128 query rows per unit take the 32-rows-per-wave kernel and 64 rows the wave-pair
+    kernel; both take weights relative to each segment's first-tile maximum. Two keys planted
+    mid-shard score about 90 (natural log units) above the rest, so those workers are
+    recomputed by the general kernel: the result still matches the oracle and flag bit 2
+    reports the recomputation."""
     from workloads import bf16_bits_from_f32
-    say("[gpu] wide MLA kernel with planted high-score keys")
-    wl = workload("mla-128h").replace(batch=2)
+    say(f"[gpu] lazy-max MLA kernel with planted high-score keys: {wl_name}")
+    wl = workload(wl_name).replace(batch=2)
     lengths = [3000, 2000]
     host = make_host_inputs(wl, lengths=lengths)
     bs = wl.block_size
