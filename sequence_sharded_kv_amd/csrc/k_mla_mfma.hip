@@ -616,7 +616,7 @@ mla_wide_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
         return mla_tr_pair(tb + r1 * 1024 + vw + 16 * ((vcq + 4 * mt) ^ wa(r1)),
                            tb + (r1 + 8) * 1024 + vw + 16 * ((vcq + 4 * mt) ^ wa(r1 + 8)));
       };
-      constexpr int kVPre = 3;  // value operand pairs in flight
+      constexpr int kVPre = 2;  // value operand pairs in flight
       bf16x8 vbuf[kVPre];
 #pragma unroll
       for (int s2 = 0; s2 < kVPre; ++s2) vbuf[s2] = vread(s2);
@@ -912,19 +912,28 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
       const int kr0 = tok_of_row(lk & 15), kq = lk >> 4;
       const int kb = kr0 * 1024, kxq = 16 * (kq ^ kr0);
       const int kbB = kRegionB + kr0 * 128, kxBq = 16 * (kq ^ (kr0 & 7));
-      f32x4 s[2];
+      // The two subtiles' chains alternate and the K reads run kPre ahead: left to the
+      // compiler, one chain ran after the other with one read in flight, each MFMA waiting on
+      // its read and on the previous MFMA.
+      auto kread = [&](int idx) -> bf16x8 {  // idx = 2 j + at
+        const int at = idx & 1, j = idx >> 1;
+        const char* p = (j < 16) ? tb + kb + 16384 * at + 256 * (j >> 2) + ((64 * (j & 3)) ^ kxq)
+                                 : tb + kbB + 2048 * at + ((64 * (j - 16)) ^ kxBq);
+        return __builtin_bit_cast(bf16x8, *(const u32x4*)p);
+      };
+      constexpr int kPre = 4;
+      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      bf16x8 kbuf[kPre];
 #pragma unroll
-      for (int at = 0; at < 2; ++at) {
-        s[at] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < kPre; ++q) kbuf[q] = kread(q);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < kMlaDqk / 32; ++j) {
-          const char* p = (j < 16) ? tb + kb + 16384 * at + 256 * (j >> 2) + ((64 * (j & 3)) ^ kxq)
-                                   : tb + kbB + 2048 * at + ((64 * (j - 16)) ^ kxBq);
-          const bf16x8 kop = __builtin_bit_cast(bf16x8, *(const u32x4*)p);
-          s[at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[j], s[at], 0, 0, 0);
-        }
+      for (int idx = 0; idx < 2 * (kMlaDqk / 32); ++idx) {
+        const bf16x8 kop = kbuf[idx % kPre];
+        if (idx + kPre < 2 * (kMlaDqk / 32)) kbuf[idx % kPre] = kread(idx + kPre);
+        s[idx & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[idx >> 1], s[idx & 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-
 
       // weights against the fixed reference; s[at][i] is MFMA row 4gq + i of subtile at
       float x[8];
@@ -967,22 +976,29 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
       const int vb = vrow0 * 1024 + 512 * hw + 8 * (vn & 1);
       const int vxq = 16 * (((8 * (vq & 1)) | ((vn & 3) >> 1)) ^ vrow0);
       const int xo = 2048 * ((vq & 1) ? pw : wv) + 16 * (vn + 32 * (vq >> 1));
+      // the weights of both k steps first, then the V operands kVPre ahead of their MFMAs
+      const bf16x8 ph[2] = {__builtin_bit_cast(bf16x8, *(const u32x4*)(xch + xo)),
+                            __builtin_bit_cast(bf16x8, *(const u32x4*)(xch + xo + 256))};
+      const bf16x8 pl[2] = {__builtin_bit_cast(bf16x8, *(const u32x4*)(xch + xo + 1024)),
+                            __builtin_bit_cast(bf16x8, *(const u32x4*)(xch + xo + 1280))};
+      auto vread = [&](int step) -> bf16x8 {  // step = 8 s2 + mt
+        const int s2 = step >> 3, mt = step & 7;
+        const char* v0 = tb + vb + 1024 * s2 + 256 * (mt >> 2) + ((32 * (mt & 3) + 16 * s2) ^ vxq);
+        return mla_tr_pair(v0, v0 + 16 * 1024);
+      };
+      constexpr int kVPre = 2;
+      bf16x8 vbuf[kVPre];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 ph = __builtin_bit_cast(bf16x8, *(const u32x4*)(xch + xo + 256 * s2));
-        const bf16x8 pl = __builtin_bit_cast(bf16x8, *(const u32x4*)(xch + xo + 1024 + 256 * s2));
+      for (int q = 0; q < kVPre; ++q) vbuf[q] = vread(q);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mp = 0; mp < 4; ++mp) {
-          const int m0 = 2 * mp, m1 = 2 * mp + 1;
-          const char* v0 = tb + vb + 1024 * s2 + 256 * (m0 >> 2) + ((32 * (m0 & 3) + 16 * s2) ^ vxq);
-          const char* v1 = tb + vb + 1024 * s2 + 256 * (m1 >> 2) + ((32 * (m1 & 3) + 16 * s2) ^ vxq);
-          const bf16x8 va = mla_tr_pair(v0, v0 + 16 * 1024);
-          const bf16x8 vbo = mla_tr_pair(v1, v1 + 16 * 1024);
-          acc[m0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, ph, acc[m0], 0, 0, 0);
-          acc[m1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vbo, ph, acc[m1], 0, 0, 0);
-          acc[m0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pl, acc[m0], 0, 0, 0);
-          acc[m1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vbo, pl, acc[m1], 0, 0, 0);
-        }
+      for (int step = 0; step < 16; ++step) {
+        const int s2 = step >> 3, mt = step & 7;
+        const bf16x8 vop = vbuf[step % kVPre];
+        if (step + kVPre < 16) vbuf[step % kVPre] = vread(step + kVPre);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, ph[s2], acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pl[s2], acc[mt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) lgkmcnt(0): the next tile's copies landed
       __syncthreads();
