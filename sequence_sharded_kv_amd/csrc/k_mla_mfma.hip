@@ -694,11 +694,16 @@ mla_wide_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
 //
 // Tile layout (36 KB, no padding, so that two tiles and the 8 KB weight exchange of each of
 // two workgroups fill the 160 KB of LDS): region A = dims 0..511, row r at 1024 r, 16-byte
-// chunk c at position c ^ (r & 15); region B = dims 512..575, row r at 32768 + 128 r, chunk c
-// at c ^ (r & 7). The copies permute the chunks (lane i of a row copy fetches chunk
-// i ^ (r & 15)). Rows keep the token permutation pi of mla_mfma_kernel, so the transposed value
-// reads of one 16-lane group (4 rows 2 apart, two chunks) hit 8 distinct 16-byte bank
-// groups, and the two groups of a half-wave (dims 64 apart) different halves of the banks.
+// chunk c at position c ^ swz_a(r), swz_a(r) = 2 (r & 15) ^ 32 ((r >> 3) & 1); region B =
+// dims 512..575, row r at 32768 + 128 r, chunk c at c ^ (r & 7). The copies permute the chunks
+// (lane i of a row copy fetches chunk i ^ swz_a(r)). LDS serves 512 bytes per clock here
+// (the bank-conflict counter agrees with that model and not with 256): the score reads of a
+// half-wave (16 rows x 2 chunks) then cover 32 distinct 16-byte bank groups. The rows keep the
+// token permutation pi of mla_mfma_kernel. A value block is dims 16 mt .. + 15 for lane groups
+// 0 and 2 and the same + 128 for groups 1 and 3, which leaves the transposed reads 2-way
+// conflicted in half of the wave (SQ_LDS_BANK_CONFLICT 3.2e8 cycles per launch against 6.4e8
+// for c ^ (r & 15)). A fully conflict-free mapping (32 consecutive dims per block, groups 16
+// dims apart) measured 2.5% slower in the same runs, for reasons the counters do not show.
 namespace pair {
 constexpr int kTile = 32;
 constexpr int kRegionB = 32 * 1024;
@@ -708,7 +713,8 @@ constexpr int kRows = kTile / kNW;               // region-A rows each wave copi
 constexpr int kXBytes = kNW * 64 * 32;           // weight exchange: 32 B per lane per wave
 constexpr float kLazy = 64.f;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
-__device__ __forceinline__ int swz_a(int r) { return r & 15; }
+// region-A chunk swizzle: bits 1-4 from the row's low four bits, bit 5 from its bit 3
+__device__ __forceinline__ int swz_a(int r) { return (2 * (r & 15)) ^ (32 * ((r >> 3) & 1)); }
 }  // namespace pair
 
 __global__ void __launch_bounds__(64 * pair::kNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -740,12 +746,12 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
   // (a few VALU operations per tile): held across the loop they would be spilled, and a
   // reload's wait on the vector memory counter would also wait for the tile copies in flight.
   // Score reads: lane (n, gq) reads row 16 at + pi(n), chunk 4 j + gq, region A at
-  //   pi(n) 1024 + 16384 at + 256 (j >> 2) + (64 (j & 3) ^ 16 (gq ^ pi(n))),
+  //   pi(n) 1024 + 16384 at + (64 j ^ 16 (gq ^ swz_a(pi(n)))),
   // region B (j = 16 + jb) at 32768 + 128 pi(n) + 2048 at + (64 jb ^ 16 (gq ^ (pi(n) & 7))).
   // Value reads, k step s2: 16-lane group gq, lane 4 i + e reads row pi(4 (s2 + 2 (gq >> 1)) +
   // i) = 8 (gq >> 1) + 2 i + s2 (+16 for the second half), the 8 bytes of dims 256 hw +
-  // 128 (mt >> 2) + 16 (mt & 3) + 64 (gq & 1) + 4 e .. + 3, at
-  //   vbase + 1024 s2 + 256 (mt >> 2) + ((32 (mt & 3) | 16 s2) ^ vx).
+  // 16 mt + 128 (gq & 1) + 4 e .. + 3, at
+  //   vbase + 1024 s2 + (32 (mt ^ s2) ^ vx).
   // Weight exchange reads: the B operand of k step s2 holds, in lane rows 0 and 2, this
   // wave's lanes 32 (gq >> 1) + 16 s2 + n and, in rows 1 and 3, the partner's.
 
@@ -910,14 +916,14 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
       int lk = lane;
       asm volatile("" : "+v"(lk));
       const int kr0 = tok_of_row(lk & 15), kq = lk >> 4;
-      const int kb = kr0 * 1024, kxq = 16 * (kq ^ kr0);
+      const int kb = kr0 * 1024, kxq = 16 * (kq ^ swz_a(kr0));
       const int kbB = kRegionB + kr0 * 128, kxBq = 16 * (kq ^ (kr0 & 7));
       // The two subtiles' chains alternate and the K reads run kPre ahead: left to the
       // compiler, one chain ran after the other with one read in flight, each MFMA waiting on
       // its read and on the previous MFMA.
       auto kread = [&](int idx) -> bf16x8 {  // idx = 2 j + at
         const int at = idx & 1, j = idx >> 1;
-        const char* p = (j < 16) ? tb + kb + 16384 * at + 256 * (j >> 2) + ((64 * (j & 3)) ^ kxq)
+        const char* p = (j < 16) ? tb + kb + 16384 * at + ((64 * j) ^ kxq)
                                  : tb + kbB + 2048 * at + ((64 * (j - 16)) ^ kxBq);
         return __builtin_bit_cast(bf16x8, *(const u32x4*)p);
       };
@@ -973,8 +979,8 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
       asm volatile("" : "+v"(lv));
       const int vn = lv & 15, vq = lv >> 4;
       const int vrow0 = 8 * (vq >> 1) + 2 * (vn >> 2);
-      const int vb = vrow0 * 1024 + 512 * hw + 8 * (vn & 1);
-      const int vxq = 16 * (((8 * (vq & 1)) | ((vn & 3) >> 1)) ^ vrow0);
+      const int vb = vrow0 * 1024 + 512 * (hw ^ (vq >> 1)) + 8 * (vn & 1);
+      const int vxq = 16 * (((16 * (vq & 1)) | ((vn & 3) >> 1)) ^ (2 * vrow0));
       const int xo = 2048 * ((vq & 1) ? pw : wv) + 16 * (vn + 32 * (vq >> 1));
       // the weights of both k steps first, then the V operands kVPre ahead of their MFMAs
       const bf16x8 ph[2] = {__builtin_bit_cast(bf16x8, *(const u32x4*)(xch + xo)),
@@ -983,7 +989,7 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
                             __builtin_bit_cast(bf16x8, *(const u32x4*)(xch + xo + 1280))};
       auto vread = [&](int step) -> bf16x8 {  // step = 8 s2 + mt
         const int s2 = step >> 3, mt = step & 7;
-        const char* v0 = tb + vb + 1024 * s2 + 256 * (mt >> 2) + ((32 * (mt & 3) + 16 * s2) ^ vxq);
+        const char* v0 = tb + vb + 1024 * s2 + ((32 * (mt ^ s2)) ^ vxq);
         return mla_tr_pair(v0, v0 + 16 * 1024);
       };
       constexpr int kVPre = 2;
@@ -1033,15 +1039,13 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
       dst_l = a.piece_lse + (int64_t)slot * a.Ru + hrow;
     }
     if (rho >= 0) {
-      // acc[mt][4 qd + i] is dim 256 hw + 128 (mt >> 2) + 16 (mt & 3) + 64 (qd >> 1) +
-      // 8 (qd & 1) + 4 (lane >> 5) + i
+      // acc[mt][4 qd + i] is dim 256 hw + 16 mt + 128 (qd >> 1) + 8 (qd & 1) + 4 (lane >> 5) + i
       const int dbase = 256 * hw + 4 * (lane >> 5);
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd)
-          *(f32x4*)(dst_o + dbase + 128 * (mt >> 2) + 16 * (mt & 3) + 64 * (qd >> 1) +
-                    8 * (qd & 1)) =
+          *(f32x4*)(dst_o + dbase + 16 * mt + 128 * (qd >> 1) + 8 * (qd & 1)) =
               f32x4{acc[mt][4 * qd], acc[mt][4 * qd + 1], acc[mt][4 * qd + 2],
                     acc[mt][4 * qd + 3]} * inv;
       if (lane < 16) *dst_l = lc > 0.f ? (mc + fast_log2(lc)) * kLn2 : kNegInf;
