@@ -704,6 +704,25 @@ mla_wide_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
 // conflicted in half of the wave (SQ_LDS_BANK_CONFLICT 3.2e8 cycles per launch against 6.4e8
 // for c ^ (r & 15)). A fully conflict-free mapping (32 consecutive dims per block, groups 16
 // dims apart) measured 2.5% slower in the same runs, for reasons the counters do not show.
+// One 16-byte-per-lane HBM -> LDS copy from a wave-uniform 64-bit base in scalar registers
+// plus a 32-bit per-lane byte offset (the SADDR form of global_load_lds_dwordx4): one VALU
+// operation per copy for the offset instead of a 64-bit address per lane. Lane i's 16 bytes
+// land at lds_addr + 16 i. The non-temporal policy, the M0 handling and the explicit waits are
+// as for dma16.
+__device__ __forceinline__ void dma16s(uint64_t sbase, uint32_t voff, uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);  // wave-uniform by contract
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(m0v)
+      : "memory");
+}
+
 namespace pair {
 constexpr int kTile = 32;
 constexpr int kRegionB = 32 * 1024;
@@ -774,7 +793,9 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
     // Token positions fit in 32 bits (max_blocks_per_seq * block_size <= INT32_MAX).
     const int32_t t0i = (int32_t)t0, t1i = (int32_t)t1;
     auto page_of = [&](int32_t tile) -> int32_t {
-      const int32_t t = tile + (lane & 31);
+      int lp = lane;
+      asm volatile("" : "+v"(lp));
+      const int32_t t = tile + (lp & 31);
       const int32_t tc = t < t1i ? t : t1i - 1;
       return brow[bs_pow2 ? (tc >> bs_shift) : tc / a.bs];
     };
@@ -791,21 +812,21 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
     auto issue_rows = [&](int k0, int k1) {
       // each row's chunk permutation is formed next to its copy: eight per-lane offsets held
       // across the tile would be spilled, and a reload's wait would also wait for the copies
-      int lx = lane;
-      asm volatile("" : "+v"(lx));
+      uint32_t lx16 = 16u * (uint32_t)lane;
+      asm volatile("" : "+v"(lx16));
       if (one) {
 #pragma unroll
         for (int k = k0; k < k1; ++k) {
           const int r = wv + k * NW;
           const uint32_t rr = (uint32_t)(r < rlast ? r : rlast);
-          dma16((const char*)(rbase + (uint64_t)(rr * rstride)) + 16 * (lx ^ swz_a(r)),
-                base_pend + r * 1024);
+          dma16s(rbase + (uint64_t)(rr * rstride), lx16 ^ (16u * (uint32_t)swz_a(r)),
+                 base_pend + r * 1024);
         }
       } else {
 #pragma unroll
         for (int k = k0; k < k1; ++k) {
           const int r = wv + k * NW;
-          dma16((const char*)row_src[k] + 16 * (lx ^ swz_a(r)), base_pend + r * 1024);
+          dma16s(row_src[k], lx16 ^ (16u * (uint32_t)swz_a(r)), base_pend + r * 1024);
         }
       }
     };
@@ -836,9 +857,8 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
           asm volatile("" : "+v"(lb));
           const int r = 8 * wv + (lb >> 3);
           const uint32_t rr = (uint32_t)(r < rlast ? r : rlast);
-          const uint64_t ra = rbase + (uint64_t)(rr * rstride);
-          dma16((const char*)ra + 1024 + 16 * ((lb & 7) ^ swz_b(r)),
-                base + kRegionB + wv * 1024);
+          dma16s(rbase, rr * rstride + 1024u + 16u * (uint32_t)((lb & 7) ^ swz_b(r)),
+                 base + kRegionB + wv * 1024);
         }
         return m;
       }
