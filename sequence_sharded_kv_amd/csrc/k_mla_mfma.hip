@@ -961,31 +961,57 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // weights against the fixed reference; s[at][i] is MFMA row 4gq + i of subtile at
+      // weights against the fixed reference; s[at][i] is MFMA row 4gq + i of subtile at. The
+      // mask is wave-uniform; a tile with every token visible (all but a segment's edges)
+      // skips the per-score masking and the -inf guards.
       float x[8];
       float tmax = kNegInf;
+      const bool full = mask == 0xFFFFFFFFu;
+      if (full) {
 #pragma unroll
-      for (int at = 0; at < 2; ++at)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = 16 * at + tok_of_row(4 * gq + i);
-          const float v = ((mask >> tok) & 1u) ? s[at][i] * a.scale_log2 : kNegInf;
-          x[4 * at + i] = v;
-          tmax = fmaxf(tmax, v);
+        for (int k = 0; k < 8; ++k) {
+          x[k] = s[k >> 2][k & 3] * a.scale_log2;
+          tmax = fmaxf(tmax, x[k]);
         }
+      } else {
+#pragma unroll
+        for (int at = 0; at < 2; ++at)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = 16 * at + tok_of_row(4 * gq + i);
+            const float v = ((mask >> tok) & 1u) ? s[at][i] * a.scale_log2 : kNegInf;
+            x[4 * at + i] = v;
+            tmax = fmaxf(tmax, v);
+          }
+      }
       tmax = quad_max(tmax);
       if (m_ref == kNegInf) m_ref = tmax;  // first valid tile of the row (O and l are zero)
       else over |= (tmax > m_ref + kLazy) ? 1 : 0;
-      float psum = 0.f;
-      bf16x8 phi, plo;
+      float pw8[8];
+      if (full) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float p = (x[k] == kNegInf) ? 0.f : fast_exp2(x[k] - m_ref);
-        psum += p;
-        const __bf16 hi = (__bf16)p;
-        phi[k] = hi;
-        plo[k] = (__bf16)(p - (float)hi);
+        for (int k = 0; k < 8; ++k) pw8[k] = fast_exp2(x[k] - m_ref);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pw8[k] = (x[k] == kNegInf) ? 0.f : fast_exp2(x[k] - m_ref);
       }
+      // bf16 high parts packed in pairs, the remainders from the unpacked highs
+      float psum = 0.f;
+      u32x4 hpk, lpk;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float p0 = pw8[2 * q], p1 = pw8[2 * q + 1];
+        psum += p0 + p1;
+        typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+        const bf16x2 h = {(__bf16)p0, (__bf16)p1};
+        const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+        const float r0 = p0 - __uint_as_float(hb << 16);
+        const float r1 = p1 - __uint_as_float(hb & 0xFFFF0000u);
+        const bf16x2 l = {(__bf16)r0, (__bf16)r1};
+        hpk[q] = hb;
+        lpk[q] = __builtin_bit_cast(uint32_t, l);
+      }
+      const bf16x8 phi = __builtin_bit_cast(bf16x8, hpk), plo = __builtin_bit_cast(bf16x8, lpk);
       l_run += psum;
 
       // hand the weights to the partner wave
