@@ -30,6 +30,13 @@ CASES = [
     ("mla-128h-t2", "mla-128h", [1200, 33], 2, dict(batch=2)),
     ("mla-32h-t3-padding", "mla-64h-b512", [600, 97], 3, dict(batch=2, num_q_heads=32)),
     ("mla-64h-t4-bs1", "mla-64h-b512", [150, 5], 4, dict(batch=2, block_size=1)),
+    # 64 rows per unit (the wave-pair kernel) from several query tokens: a wave's partner
+    # holds the other token's rows, or padding rows (16 heads x 3 tokens = 48 of 64)
+    ("mla-32h-t2-pair", "mla-64h-b512", [1300, 45], 2, dict(batch=2, num_q_heads=32)),
+    ("mla-16h-t3-pair-padding", "mla-64h-b512", [800, 130, 2], 3, dict(batch=3,
+                                                                      num_q_heads=16)),
+    ("mla-16h-t4-pair-bs16", "mla-64h-b512", [700, 64], 4, dict(batch=2, num_q_heads=16,
+                                                               block_size=16)),
     ("gqa-g16-t2", "gqa-g16", [3000, 1, 100], 2, dict(batch=3)),
     ("gqa-g4-d64-t4", "gqa-g16", [900, 3], 4, dict(batch=2, num_q_heads=16, head_dim_qk=64,
                                                     head_dim_v=64)),
