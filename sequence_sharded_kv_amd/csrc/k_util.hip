@@ -64,7 +64,8 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
     int64_t u = base + tid;
     int32_t cnt = 0;
     if (u < U) {
-      int64_t bsi = u / units_per_bs;
+      // U * max_blocks fits in 32 bits (checked by the host plan), so unit indices do too
+      const int64_t bsi = (int64_t)((uint32_t)u / (uint32_t)units_per_bs);
       int64_t a = bounds[2 * bsi], e = bounds[2 * bsi + 1];
       int64_t a0 = a, e0 = e;
       if (a < 0) a = 0;
@@ -72,11 +73,14 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
       if (a > cap) a = cap;
       if (e < a) e = a;
       if (a != a0 || e != e0) my_flag |= kFlagBoundClamped;
-      if (u % units_per_bs == 0) {
+      if ((uint32_t)u - (uint32_t)bsi * (uint32_t)units_per_bs == 0) {
         ubounds[2 * bsi] = (int32_t)a;
         ubounds[2 * bsi + 1] = (int32_t)e;
       }
-      cnt = (e > a) ? (int32_t)((e + bs - 1) / bs - a / bs) : 0;
+      // 0 <= a <= e <= cap <= INT32_MAX: 32-bit page arithmetic
+      cnt = (e > a) ? (int32_t)(((uint32_t)e + (uint32_t)bs - 1u) / (uint32_t)bs -
+                                (uint32_t)a / (uint32_t)bs)
+                    : 0;
     }
     // inclusive scan within the wave
     int lane = tid & 63, wv = tid >> 6;
@@ -114,12 +118,22 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
     qend[b] = end - Tq;
   }
   const int64_t T = carry;
+  // worker_of in 32-bit unsigned arithmetic when (T + 1) * P fits (the same quotients; the
+  // 64-bit divisions cost more than the rest of this pass)
+  const bool narrow = (T + 1) * (int64_t)P < ((int64_t)1 << 32);
+  auto owner = [&](int64_t g) -> int32_t {
+    if (narrow) {
+      const uint32_t w = ((uint32_t)(g + 1) * (uint32_t)P - 1u) / (uint32_t)T;
+      return (int32_t)(w < (uint32_t)(P - 1) ? w : (uint32_t)(P - 1));
+    }
+    return worker_of(T, P, g);
+  };
   for (int64_t u = tid; u < U; u += kSchedThreads) {
     const int64_t p0 = pre[u], p1 = pre[u + 1];
     int32_t w0 = -1, w1 = -1;
     if (p1 > p0) {
-      w0 = worker_of(T, P, p0);
-      w1 = worker_of(T, P, p1 - 1);
+      w0 = owner(p0);
+      w1 = owner(p1 - 1);
       if (w0 == w1) continue;  // written whole by its worker
     }
     const int32_t k = atomicAdd(&fin_count, 1);
