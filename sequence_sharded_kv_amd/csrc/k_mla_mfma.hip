@@ -688,9 +688,11 @@ mla_wide_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
 //     8 accumulator blocks of 32 dims x 32 rows, 32 MFMAs per tile instead of 64.
 // Like mla_wide_kernel it takes the reference max from the first tile with a valid token and
 // never rescales; a worker whose scores outrun it by kLazy (exp2 units) is recomputed by
-// mla_mfma_kernel<4> afterwards. All copies of the next tile are queued before the scores:
-// with the value product this short the copies, not the matrix unit, pace the loop (queueing
-// half of them after the scores, as mla_mfma_kernel does, measured 7% slower here).
+// mla_mfma_kernel<4> afterwards. Three of a wave's eight row copies of the next tile and its
+// region-B copy are queued before the scores, the other five after them: a wave stalls while
+// the memory pipeline is full, and an s_memtime breakdown put 26% of a wave-tile in queueing
+// the copies when all nine went first. With 3 first the kernel ran 1-1.5% faster than with 8,
+// 4 or 2; 5 was no faster and 6 slower.
 //
 // Tile layout (36 KB, no padding, so that two tiles and the 8 KB weight exchange of each of
 // two workgroups fill the 160 KB of LDS): region A = dims 0..511, row r at 1024 r, 16-byte
@@ -729,6 +731,7 @@ constexpr int kRegionB = 32 * 1024;
 constexpr int kTileBytes = kRegionB + 32 * 128;  // 36864
 constexpr int kNW = 4;
 constexpr int kRows = kTile / kNW;               // region-A rows each wave copies per tile
+constexpr int kQ0 = 3;                           // of them queued before the scores
 constexpr int kXBytes = kNW * 64 * 32;           // weight exchange: 32 B per lane per wave
 constexpr float kLazy = 64.f;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
@@ -830,7 +833,7 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
         }
       }
     };
-    auto issue_tile = [&](int32_t tile, int buf) -> uint32_t {
+    auto issue_tile = [&](int32_t tile, int buf, int nrows) -> uint32_t {
       const int32_t blk = blk_next;
       if (tile + kTile < t1i) blk_next = page_of(tile + kTile);
       const uint32_t base = lds_u32(&lds[buf * kTileBytes]);
@@ -851,7 +854,7 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
         rlast = t1i - 1 - tile;
         if (!page_ok) bad = 1;
         const uint32_t m = (uint32_t)__ballot(page_ok && lane < kTile && tile + lane < t1i);
-        issue_rows(0, kRows);
+        issue_rows(0, nrows);
         {
           int lb = lane;
           asm volatile("" : "+v"(lb));
@@ -920,7 +923,7 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
       for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
     float m_ref = kNegInf, l_run = 0.f;
 
-    uint32_t mask_next = issue_tile(t0i, 0);
+    uint32_t mask_next = issue_tile(t0i, 0, kRows);
     __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) lgkmcnt(0): the copies of the first tile
     __syncthreads();
     int cur = 0;
@@ -929,7 +932,7 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
       const uint32_t mask =
           mask_next & (dl < 0 ? 0u : dl >= kTile - 1 ? 0xFFFFFFFFu : (2u << dl) - 1u);
       const bool more = tile + kTile < t1i;
-      if (more) mask_next = issue_tile(tile + kTile, cur ^ 1);
+      if (more) mask_next = issue_tile(tile + kTile, cur ^ 1, kQ0);
       const char* tb = &lds[cur * kTileBytes];
 
       // S^T = K . Q^T for the two 16-row subtiles
@@ -961,6 +964,7 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
         __builtin_amdgcn_sched_barrier(0);
       }
 
+      if (more && one) issue_rows(kQ0, kRows);  // the rest of a one-page tile's row copies
       // weights against the fixed reference; s[at][i] is MFMA row 4gq + i of subtile at. The
       // mask is wave-uniform; a tile with every token visible (all but a segment's edges)
       // skips the per-score masking and the -inf guards.
@@ -974,11 +978,15 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
           tmax = fmaxf(tmax, x[k]);
         }
       } else {
+        // per-lane token positions formed here (held across the loop they would be spilled)
+        int lm = lane;
+        asm volatile("" : "+v"(lm));
+        const int gqm = lm >> 4;
 #pragma unroll
         for (int at = 0; at < 2; ++at)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int tok = 16 * at + tok_of_row(4 * gq + i);
+            const int tok = 16 * at + tok_of_row(4 * gqm + i);
             const float v = ((mask >> tok) & 1u) ? s[at][i] * a.scale_log2 : kNegInf;
             x[4 * at + i] = v;
             tmax = fmaxf(tmax, v);
