@@ -17,7 +17,7 @@ constexpr int32_t kWsZeroWords = 512;  // 2 KB of zeros
 // Flag bits in the workspace's sticky device flag word.
 constexpr int32_t kFlagBoundClamped = 1;
 constexpr int32_t kFlagBadBlock = 2;
-constexpr int32_t kFlagRecomputed = 4;  // a worker's range was recomputed (see mla_wide_kernel)
+constexpr int32_t kFlagRecomputed = 4;  // a worker's range was recomputed (see mla_pair_kernel)
 
 // Work is split stream-K style: every (unit, page) pair is one page of work, the pages of
 // all units are concatenated in unit order, and worker w takes the contiguous range

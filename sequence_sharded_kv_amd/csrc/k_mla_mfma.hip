@@ -337,348 +337,13 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row, const int32_t* __
   if (bad) atomicOr(a.flags, kFlagBadBlock);
 }
 
-// ---------------------------------------------------------------- 32 rows per wave
-// For 128 query rows per unit (128 heads, or several query tokens of 32 or 64 heads) one
-// workgroup per CU is all the registers allow, so the tile copies alone would leave the
-// pipeline one tile deep. This kernel gives each of the 4 waves 32 rows and both whole
-// contractions (576 score dims, 512 value dims) on v_mfma_f32_32x32x16_bf16, which does twice
-// the work of the 16x16x32 form in the same time, and streams tiles through a four-slot ring
-// filled three tiles ahead.
-//
-// The O accumulator (32 rows x 512 dims, fp32) fills the 256 accumulation registers. Scaling
-// it when the running max moves would cost 768 instructions per tile, so the reference max is
-// fixed by the first tile with a valid token (the accumulator and the sum are still zero
-// then) and weights exp2(x - ref) are taken as they come: they stay finite while x <= ref +
-// 64 in exp2 units. A score beyond that marks the worker in `redo`, and the 16-rows-per-wave
-// kernel recomputes that worker's whole range afterwards (same units, same pieces).
-//
-// Tile layout (36 KB, no padding): region A = dims 0..511, row r at 1024 r, 16-byte chunk c
-// at position c ^ wa(r), wa(r) = ((r & 3) << 2) | ((r >> 2) & 3); region B = dims 512..575, row
-// r at 32768 + 128 r, chunk c at position c ^ wb(r), wb(r) = (r >> 1) & 7. The score reads
-// (32 rows x 16 bytes) and the transposed value reads (4 rows x 64 bytes per half-wave) then
-// hit distinct banks. The copies permute the chunks (lane i of a row copy fetches chunk
-// i ^ wa(r)).
-namespace wide {
-constexpr int kRegionB = 32 * 1024;
-constexpr int kTileBytes = kRegionB + 32 * 128;  // 36864
-constexpr int kSlots = 4;
-constexpr int kNW = 4;
-constexpr int kDma = 9;          // copies per wave per tile: 8 region-A rows, 1 region-B block
-constexpr float kLazy = 64.f;    // exp2 units a score may exceed the reference max by
-__device__ __forceinline__ int wa(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int wb(int r) { return (r >> 1) & 7; }
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-}  // namespace wide
-
-__global__ void __launch_bounds__(64 * wide::kNW) __attribute__((amdgpu_waves_per_eu(1, 1)))
-mla_wide_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restrict__ redo) {
-  using namespace wide;
-  __shared__ __attribute__((aligned(1024))) char lds[kSlots * kTileBytes];
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
-  const int g = lane >> 5;          // lane half: k slice of the 32x32x16 operand layouts
-  const int c32 = lane & 31;        // operand row / column index
-  const int32_t w = blockIdx.x;
-  if (w >= a.P) return;
-  const uint16_t* __restrict__ Q = (const uint16_t*)a.q;
-  const char* __restrict__ Kc = (const char*)a.k;
-  const int64_t T_pages = a.pre[a.U];
-  const int64_t g0 = worker_begin(T_pages, a.P, w), g1 = worker_begin(T_pages, a.P, w + 1);
-  if (g0 >= g1) return;
-  int32_t u = find_unit(a.pre, a.U, g0);
-  int64_t gg = g0;
-  int32_t bad = 0, over = 0;
-  const bool bs_pow2 = (a.bs & (a.bs - 1)) == 0;
-  const int bs_shift = __builtin_ctz((unsigned)a.bs);
-  const uint32_t lds0 = lds_u32(&lds[0]);
-
-  // transposed value reads: 16-lane group q4, lane L reads rows 16 kk + 4 (q4 >> 1) + (L >> 2)
-  // and + 8, chunk 4 mt + 2 (q4 & 1) + ((L & 3) >> 1), byte 8 (L & 1) of the chunk
-  const int q4 = lane >> 4, L = lane & 15;
-  const int vr = 4 * (q4 >> 1) + (L >> 2);
-  const int vc = 2 * (q4 & 1) + ((L & 3) >> 1);
-  const int vw = 8 * (L & 1);
-
-  while (gg < g1) {
-    while ((int64_t)a.pre[u + 1] <= gg) ++u;
-    const int64_t up0 = a.pre[u], up1 = a.pre[u + 1];
-    const int64_t sg1 = up1 < g1 ? up1 : g1;
-    const int32_t bsi = u / a.NRg, rg = u - bsi * a.NRg;  // (request, shard), row group
-    const int32_t b = bsi / a.S;
-    const int64_t ta = a.ubounds[2 * bsi], te = a.ubounds[2 * bsi + 1];
-    const int64_t pa = ta / a.bs;
-    int64_t t0 = (pa + (gg - up0)) * a.bs, t1 = (pa + (sg1 - up0)) * a.bs;
-    if (t0 < ta) t0 = ta;
-    if (t1 > te) t1 = te;
-    const bool whole = (gg == up0) && (sg1 == up1);
-    const bool first = (gg == g0);
-    const int32_t* brow = a.block_table + (int64_t)b * a.max_blocks;
-    const int32_t t0i = (int32_t)t0, t1i = (int32_t)t1;
-    const int32_t ntiles = (t1i - t0i + 31) / 32;  // >= 1
-    auto page_idx = [&](int32_t t) -> int32_t { return bs_pow2 ? (t >> bs_shift) : t / a.bs; };
-    const int32_t plast_seg = page_idx(t1i - 1);
-
-    // This wave's 32 query rows (32 | Hq: one query token per wave) and the last context
-    // position they may see; rows past R are padding and not stored.
-    int32_t jq = 0;
-    const int32_t rho = unit_row(a, 0, rg, 32 * wv + c32, &jq);
-    const bool row_ok = rho >= 0;
-    const int32_t lim = a.Tq == 1 ? INT32_MAX : __builtin_amdgcn_readfirstlane(a.qend[b] + jq);
-
-    // Block ids of the segment's pages, 64 at a time: lane j holds the id of page pchunk + j.
-    // Refilled (one load, waited for) only when a tile leaves the window.
-    int32_t pchunk = -1, pid = -1;
-    auto ensure_pages = [&](int32_t pfirst, int32_t plast) {
-      if (pchunk < 0 || plast >= pchunk + 64) {
-        pchunk = pfirst;
-        const int32_t pp = pchunk + lane;
-        pid = (pp <= plast_seg) ? brow[pp] : -1;
-        asm volatile("" : "+v"(pid));  // keep the wait for this load inside the branch
-      }
-    };
-
-    // Queue tile i into slot i % kSlots: this wave's region-A rows wv + 4k (the first
-    // `nrows`; the rest through issue_rest, after the scores) and its region-B block. The
-    // source addresses stay in one lane each (lane r: row r) until their copy is queued.
-    uint64_t rowaddr_pend = 0;
-    uint32_t base_pend = 0;
-    auto issue_rows = [&](int k0, int k1) {
-      int lx = lane;
-      uint32_t bp = base_pend;
-      asm volatile("" : "+v"(lx), "+s"(bp));  // offsets formed next to their copies
-#pragma unroll
-      for (int k = k0; k < k1; ++k) {
-        const int r = wv + kNW * k;
-        const uint64_t src = readlane_u64(rowaddr_pend, r);
-        dma16((const char*)src + 16 * (lx ^ wa(r)), bp + r * 1024);
-      }
-    };
-    auto issue_tile = [&](int32_t i, int nrows) -> uint32_t {
-      const int32_t tile = t0i + 32 * i;
-      const int32_t tl = (tile + 31 < t1i ? tile + 31 : t1i - 1);
-      const int32_t pfirst = page_idx(tile), plast = page_idx(tl);
-      ensure_pages(pfirst, plast);
-      const int32_t t = tile + (lane & 31);
-      const int32_t tc = t < t1i ? t : t1i - 1;
-      const int32_t mypage = page_idx(tc);
-      int32_t blk = -1;
-      for (int32_t pg = pfirst; pg <= plast; ++pg) {
-        const int32_t id = __builtin_amdgcn_readlane(pid, pg - pchunk);
-        blk = (mypage == pg) ? id : blk;
-      }
-      uint64_t rowaddr = (uint64_t)zero_row;
-      bool valid = false, masked = false;
-      if (lane < 32) {
-        const bool page_ok = blk >= 0 && blk < a.num_blocks;
-        const uint32_t slot = bs_pow2 ? (uint32_t)(tc & (a.bs - 1)) : (uint32_t)(tc % a.bs);
-        const uint32_t row = (uint32_t)blk * (uint32_t)a.bs + slot;
-        if (page_ok) rowaddr = (uint64_t)Kc + (uint64_t)row * (kMlaDqk * 2);
-        valid = page_ok && t < t1i;
-        masked = !page_ok;
-      }
-      bad |= __any(masked) ? 1 : 0;
-      const uint32_t mask = (uint32_t)__ballot(valid);
-      rowaddr_pend = rowaddr;
-      base_pend = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((i % kSlots) * kTileBytes));
-      issue_rows(0, nrows);
-      {
-        // region B: rows 8 wv + lane / 8, chunk position lane & 7
-        uint64_t ra = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint64_t aj = readlane_u64(rowaddr, 8 * wv + j);
-          ra = ((lane >> 3) == j) ? aj : ra;
-        }
-        const int r = 8 * wv + (lane >> 3);
-        dma16((const char*)ra + 1024 + 16 * ((lane & 7) ^ wb(r)),
-              base_pend + kRegionB + wv * 1024);
-      }
-      return mask;
-    };
-    // at most `later` tiles' copies of this wave still in flight
-    auto wait_tiles = [&](int32_t later) {
-      if (later >= 2)
-        __builtin_amdgcn_s_waitcnt(((2 * kDma) & 15) | (((2 * kDma) >> 4) << 14) | (7 << 4) |
-                                   (15 << 8));
-      else if (later == 1)
-        __builtin_amdgcn_s_waitcnt(kDma | (7 << 4) | (15 << 8));
-      else
-        __builtin_amdgcn_s_waitcnt(0);
-    };
-
-    // Q^T as the B operand: lane holds q[row][16 ks + 8 g .. +8]
-    bf16x8 qop[36];
-    {
-      const uint16_t* qrow = Q + ((int64_t)b * a.R + (row_ok ? rho : 0)) * kMlaDqk + 8 * g;
-      u32x4 raw[36];
-#pragma unroll
-      for (int ks = 0; ks < 36; ++ks) raw[ks] = *(const u32x4*)(qrow + 16 * ks);
-#pragma unroll
-      for (int ks = 0; ks < 36; ++ks) {
-        asm volatile("" : "+v"(raw[ks]));  // resident: no reload inside the tile loop
-        qop[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
-      }
-    }
-
-    f32x16 acc[16];
-#pragma unroll
-    for (int mt = 0; mt < 16; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
-    float m_ref = kNegInf, l_run = 0.f;
-
-    // prologue: three tiles queued, the first landed
-    uint32_t maskv = 0;  // lane s: valid-token mask of the tile in slot s
-    int32_t issued = 0;
-    for (int k = 0; k < kSlots - 1; ++k)
-      if (issued < ntiles) {
-        const uint32_t m = issue_tile(issued, 8);
-        maskv = (lane == issued % kSlots) ? m : maskv;
-        ++issued;
-      }
-    wait_tiles(issued - 1);
-    __syncthreads();
-
-    for (int32_t i = 0; i < ntiles; ++i) {
-      const bool more = issued < ntiles;
-      if (more) {
-        const uint32_t m = issue_tile(issued, 4);
-        maskv = (lane == issued % kSlots) ? m : maskv;
-      }
-      const int32_t tile = t0i + 32 * i;
-      const char* tb = &lds[(i % kSlots) * kTileBytes];
-      const int32_t dl = lim - tile;
-      const uint32_t mask = __builtin_amdgcn_readlane(maskv, i % kSlots) &
-                            (dl < 0 ? 0u : dl >= 31 ? 0xFFFFFFFFu : (2u << dl) - 1u);
-
-      // S[32 tok x 32 rows] = K . Q^T over all 576 dims, one accumulator chain
-      int fq = wa(c32), fbq = wb(c32);
-      asm volatile("" : "+v"(fq), "+v"(fbq));
-      const char* krowA = tb + c32 * 1024;
-      const char* krowB = tb + kRegionB + c32 * 128;
-      auto kread = [&](int ks) -> bf16x8 {
-        const int c = 2 * ks + g;
-        const char* p = ks < 32 ? krowA + 16 * (c ^ fq) : krowB + 16 * ((c - 64) ^ fbq);
-        return __builtin_bit_cast(bf16x8, *(const u32x4*)p);
-      };
-      f32x16 st;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = 0.f;
-      constexpr int kPre = 4;  // score reads in flight
-      bf16x8 kbuf[kPre];
-#pragma unroll
-      for (int ks = 0; ks < kPre; ++ks) kbuf[ks] = kread(ks);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = 0; ks < 36; ++ks) {
-        const bf16x8 kop = kbuf[ks % kPre];
-        if (ks + kPre < 36) kbuf[ks % kPre] = kread(ks + kPre);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], st, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (more) { issue_rows(4, 8); ++issued; }
-
-      // softmax weights against the fixed reference; st[r] is token 8 (r / 4) + 4 g + r % 4
-      float x[16];
-      float tmax = kNegInf;
-      const uint32_t hmask = mask >> (4 * g);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        x[r] = ((hmask >> (8 * (r >> 2) + (r & 3))) & 1u) ? st[r] * a.scale_log2 : kNegInf;
-        tmax = fmaxf(tmax, x[r]);
-      }
-      {
-        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
-                                                   false, false);
-        tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      if (m_ref == kNegInf) m_ref = tmax;   // first valid tile of the row (O and l are zero)
-      else over |= __any(tmax > m_ref + kLazy) ? 1 : 0;
-      float psum = 0.f;
-      bf16x8 phi[2], plo[2];
-      auto weight = [&](int r) {  // p of score r: bf16 high part and remainder
-        const float pv = (x[r] == kNegInf) ? 0.f : fast_exp2(x[r] - m_ref);
-        psum += pv;
-        const __bf16 hi = (__bf16)pv;
-        phi[r >> 3][r & 7] = hi;
-        plo[r >> 3][r & 7] = (__bf16)(pv - (float)hi);
-      };
-#pragma unroll
-      for (int r = 0; r < 8; ++r) weight(r);
-
-      // O^T[512 dv x 32 rows] += V^T . P over two 16-token k steps; the weights of the
-      // second step are formed between the MFMAs of the first
-      int vcq = vc;
-      asm volatile("" : "+v"(vcq));
-      auto vread = [&](int step) -> bf16x8 {  // step = 16 kk + mt
-        const int kk = step >> 4, mt = step & 15;
-        const int r1 = 16 * kk + vr;
-        return mla_tr_pair(tb + r1 * 1024 + vw + 16 * ((vcq + 4 * mt) ^ wa(r1)),
-                           tb + (r1 + 8) * 1024 + vw + 16 * ((vcq + 4 * mt) ^ wa(r1 + 8)));
-      };
-      constexpr int kVPre = 2;  // value operand pairs in flight
-      bf16x8 vbuf[kVPre];
-#pragma unroll
-      for (int s2 = 0; s2 < kVPre; ++s2) vbuf[s2] = vread(s2);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s2 = 0; s2 < 32; ++s2) {
-        const int kk = s2 >> 4, mt = s2 & 15;
-        const bf16x8 vop = vbuf[s2 % kVPre];
-        if (s2 + kVPre < 32) vbuf[s2 % kVPre] = vread(s2 + kVPre);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, phi[kk], acc[mt], 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, plo[kk], acc[mt], 0, 0, 0);
-        if (kk == 0 && mt < 8) weight(8 + mt);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      l_run += psum;
-      // tile i + 1 has landed and every wave is past tile i (its slot is refilled next)
-      wait_tiles(issued - (i + 2));
-      __syncthreads();
-    }
-
-    // finalise: l over the two lanes of row c32
-    float l = l_run;
-    {
-      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false,
-                                                 false);
-      l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    }
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    float* dst_o;
-    float* dst_l;
-    if (whole) {
-      dst_o = a.part_o + ((int64_t)bsi * a.R + rho) * kMlaDv;
-      dst_l = a.part_lse + (int64_t)bsi * a.R + rho;
-    } else {
-      const int32_t slot = piece_slot(w, first);
-      dst_o = a.piece_o + ((int64_t)slot * a.Ru + 32 * wv + c32) * kMlaDv;
-      dst_l = a.piece_lse + (int64_t)slot * a.Ru + 32 * wv + c32;
-    }
-    if (row_ok) {
-#pragma unroll
-      for (int mt = 0; mt < 16; ++mt)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          *(f32x4*)(dst_o + 32 * mt + 8 * r4 + 4 * g) =
-              f32x4{acc[mt][4 * r4], acc[mt][4 * r4 + 1], acc[mt][4 * r4 + 2],
-                    acc[mt][4 * r4 + 3]} * inv;
-      if (g == 0) *dst_l = l > 0.f ? (m_ref + fast_log2(l)) * kLn2 : kNegInf;
-    }
-    gg = sg1;
-  }
-  if (bad && lane == 0) atomicOr(a.flags, kFlagBadBlock);
-  if (over && lane == 0) {
-    redo[w] = 1;
-    atomicOr(a.flags, kFlagRecomputed);
-  }
-}
-
-// ---------------------------------------------------------------- pairs of waves, 64 rows
-// For 64 query rows per unit (64 heads, the agent-style decode batch) at two workgroups per
-// CU. The 16x16x32 bf16 MFMA form runs at about half the rate of 32x32x16 here, and the value
-// product (weights split into a bf16 high part and a remainder for accuracy) is two thirds of
-// the matrix work, so this kernel moves the value product onto 32x32x16:
+// ---------------------------------------------------------------- pairs of waves
+// For 64 query rows per unit (64 heads, the agent-style decode batch) with 4 waves and two
+// workgroups per CU, and for 128 rows (128 heads, or several query tokens of 32 or 64 heads)
+// with 8 waves and one workgroup per CU. The 16x16x32 bf16 MFMA form runs at about half the
+// rate of 32x32x16 here, and the value product (weights split into a bf16 high part and a
+// remainder for accuracy) is two thirds of the matrix work, so this kernel moves the value
+// product onto 32x32x16:
 //   - each wave scores its own 16 rows against the tile exactly as mla_mfma_kernel does
 //     (16x16x32, K from LDS, Q resident);
 //   - waves 2p and 2p + 1 form a pair. Each writes its weights (high part and remainder, 32 B
@@ -686,16 +351,22 @@ mla_wide_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
 //     whose columns 0..15 are its own rows and 16..31 its partner's;
 //   - wave 2p + h accumulates O^T for the pair's 32 rows over value dims [256 h, 256 h + 256):
 //     8 accumulator blocks of 32 dims x 32 rows, 32 MFMAs per tile instead of 64.
-// Like mla_wide_kernel it takes the reference max from the first tile with a valid token and
-// never rescales; a worker whose scores outrun it by kLazy (exp2 units) is recomputed by
-// mla_mfma_kernel<4> afterwards. Three of a wave's eight row copies of the next tile and its
-// region-B copy are queued before the scores, the other five after them: a wave stalls while
-// the memory pipeline is full, and an s_memtime breakdown put 26% of a wave-tile in queueing
+// The accumulator (8 blocks of 16 registers) fills the accumulation registers, and scaling
+// it whenever a row's running max moves would cost more than the value product itself. The
+// reference max is therefore fixed by the first tile with a valid token (the accumulator and
+// the sum are still zero then) and weights exp2(x - ref) are taken as they come: they stay
+// finite while x <= ref + kLazy in exp2 units. A score beyond that marks the worker in
+// `redo`, and mla_mfma_kernel<NW> recomputes that worker's whole range afterwards (same
+// units, same pieces). With 4 waves, three of a wave's eight row copies of the next tile and
+// its region-B copy are queued before the scores, the other five after them: a wave stalls
+// while the memory pipeline is full, and an s_memtime breakdown put 26% of a wave-tile in queueing
 // the copies when all nine went first. With 3 first the kernel ran 1-1.5% faster than with 8,
-// 4 or 2; 5 was no faster and 6 slower.
+// 4 or 2; 5 was no faster and 6 slower. With 8 waves a wave copies four rows (two first) and
+// waves 0-3 the region-B blocks; on 128 rows this measured 9-10% faster than a kernel with
+// 32 rows per wave on 32x32x16 for both contractions and a four-tile ring.
 //
 // Tile layout (36 KB, no padding, so that two tiles and the 8 KB weight exchange of each of
-// two workgroups fill the 160 KB of LDS): region A = dims 0..511, row r at 1024 r, 16-byte
+// two 4-wave workgroups fill the 160 KB of LDS): region A = dims 0..511, row r at 1024 r, 16-byte
 // chunk c at position c ^ swz_a(r), swz_a(r) = 2 (r & 15) ^ 32 ((r >> 3) & 1); region B =
 // dims 512..575, row r at 32768 + 128 r, chunk c at c ^ (r & 7). The copies permute the chunks
 // (lane i of a row copy fetches chunk i ^ swz_a(r)). LDS serves 512 bytes per clock here
@@ -729,20 +400,23 @@ namespace pair {
 constexpr int kTile = 32;
 constexpr int kRegionB = 32 * 1024;
 constexpr int kTileBytes = kRegionB + 32 * 128;  // 36864
-constexpr int kNW = 4;
-constexpr int kRows = kTile / kNW;               // region-A rows each wave copies per tile
-constexpr int kQ0 = 3;                           // of them queued before the scores
-constexpr int kXBytes = kNW * 64 * 32;           // weight exchange: 32 B per lane per wave
+template <int NW>  // waves per workgroup (16 rows each)
+struct Cfg {
+  static constexpr int kRows = kTile / NW;      // region-A rows each wave copies per tile
+  static constexpr int kQ0 = NW == 4 ? 3 : 2;   // of them queued before the scores
+  static constexpr int kXBytes = NW * 64 * 32;  // weight exchange: 32 B per lane per wave
+};
 constexpr float kLazy = 64.f;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 // region-A chunk swizzle: bits 1-4 from the row's low four bits, bit 5 from its bit 3
 __device__ __forceinline__ int swz_a(int r) { return (2 * (r & 15)) ^ (32 * ((r >> 3) & 1)); }
 }  // namespace pair
 
-__global__ void __launch_bounds__(64 * pair::kNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int NW>  // 4 waves for 64 rows per unit (two workgroups per CU), 8 for 128 (one)
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restrict__ redo) {
   using namespace pair;
-  constexpr int NW = kNW;
+  constexpr int kRows = Cfg<NW>::kRows, kQ0 = Cfg<NW>::kQ0, kXBytes = Cfg<NW>::kXBytes;
   __shared__ __attribute__((aligned(1024))) char lds[2 * kTileBytes + kXBytes];
   char* const xch = &lds[2 * kTileBytes];
   const int lane = threadIdx.x & 63;
@@ -855,7 +529,7 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
         if (!page_ok) bad = 1;
         const uint32_t m = (uint32_t)__ballot(page_ok && lane < kTile && tile + lane < t1i);
         issue_rows(0, nrows);
-        {
+        if (NW == 4 || wv < 4) {  // region B: four 1 KB blocks of 8 rows
           int lb = lane;
           asm volatile("" : "+v"(lb));
           const int r = 8 * wv + (lb >> 3);
@@ -885,7 +559,7 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
 #pragma unroll
       for (int k = 0; k < kRows; ++k) row_src[k] = readlane_u64(rowaddr, wv + k * NW);
       issue_rows(0, kRows);
-      {
+      if (NW == 4 || wv < 4) {
         // lane covers row 8 wv + lane / 8: pick its address among the eight rows' addresses
         uint64_t ra = 0;
 #pragma unroll
@@ -1132,22 +806,18 @@ int32_t mla_mfma_workers(int device, int32_t Ru, int32_t max_workers) {
 
 hipError_t launch_mla_mfma(const AttnArgs& a, hipStream_t stream) {
   const char* zr = a.zero_row;
-  if (a.Ru == 128 && a.Hq % 32 == 0) {
-    // 32 rows per wave; workers whose scores outran the fixed reference are recomputed by
-    // the 16-rows-per-wave kernel (same worker count: one workgroup per CU for both)
-    hipLaunchKernelGGL(mla_wide_kernel, dim3(a.P), dim3(64 * wide::kNW), 0, stream, a, zr,
-                       a.redo);
-    hipLaunchKernelGGL((mla_mfma_kernel<8>), dim3(a.P), dim3(512), 0, stream, a, zr,
-                       (const int32_t*)a.redo);
-    return hipGetLastError();
-  }
-  if (a.Ru == 64) {
+  if (a.Ru == 64 || a.Ru == 128) {
     // pairs of waves share the value product; workers whose scores outran the fixed
     // reference are recomputed by the 16-rows-per-wave kernel (same worker count)
-    hipLaunchKernelGGL(mla_pair_kernel, dim3(a.P), dim3(64 * pair::kNW), 0, stream, a, zr,
-                       a.redo);
-    hipLaunchKernelGGL((mla_mfma_kernel<4>), dim3(a.P), dim3(256), 0, stream, a, zr,
-                       (const int32_t*)a.redo);
+    if (a.Ru == 64) {
+      hipLaunchKernelGGL((mla_pair_kernel<4>), dim3(a.P), dim3(256), 0, stream, a, zr, a.redo);
+      hipLaunchKernelGGL((mla_mfma_kernel<4>), dim3(a.P), dim3(256), 0, stream, a, zr,
+                         (const int32_t*)a.redo);
+    } else {
+      hipLaunchKernelGGL((mla_pair_kernel<8>), dim3(a.P), dim3(512), 0, stream, a, zr, a.redo);
+      hipLaunchKernelGGL((mla_mfma_kernel<8>), dim3(a.P), dim3(512), 0, stream, a, zr,
+                         (const int32_t*)a.redo);
+    }
     return hipGetLastError();
   }
   const int32_t* none = nullptr;

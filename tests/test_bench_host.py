@@ -61,8 +61,9 @@ def test_kernel_family_follows_the_row_count(bench):
     assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=32), 1) == "mla"
     assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=32), 2) == "mla-pair"
     assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=16), 3) == "mla-pair"
-    assert bench.kernel_family(workload("mla-64h-b512"), 2) == "mla-wide"
-    assert bench.kernel_family(workload("mla-128h"), 1) == "mla-wide"
+    assert bench.kernel_family(workload("mla-64h-b512"), 2) == "mla-pair"   # 128 rows, 8 waves
+    assert bench.kernel_family(workload("mla-128h"), 1) == "mla-pair"
+    assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=16), 5) == "mla-pair"
     assert bench.kernel_family(workload("gqa-g16"), 1) == "gqa-mfma"
     assert bench.kernel_family(workload("gqa-g16"), 2) == "gqa-chunk"
     assert bench.kernel_family(workload("gqa-long"), 2) == "gqa-mfma"   # 8 x 2 = 16 rows

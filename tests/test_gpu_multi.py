@@ -37,6 +37,13 @@ CASES = [
                                                                       num_q_heads=16)),
     ("mla-16h-t4-pair-bs16", "mla-64h-b512", [700, 64], 4, dict(batch=2, num_q_heads=16,
                                                                block_size=16)),
+    # 128 rows per unit (the 8-wave pair kernel): 16 heads x 5 tokens = 80 of 128 rows, two
+    # pages per tile, and 32 heads x 3 tokens with a non-power-of-two page
+    ("mla-16h-t5-pair8-padding", "mla-64h-b512", [900, 70, 3], 5, dict(batch=3,
+                                                                       num_q_heads=16)),
+    ("mla-128h-pair8-bs16", "mla-128h", [1100, 40], 1, dict(batch=2, block_size=16)),
+    ("mla-32h-t3-pair8-bs48", "mla-64h-b512", [1000, 95], 3, dict(batch=2, num_q_heads=32,
+                                                                block_size=48)),
     ("gqa-g16-t2", "gqa-g16", [3000, 1, 100], 2, dict(batch=3)),
     ("gqa-g4-d64-t4", "gqa-g16", [900, 3], 4, dict(batch=2, num_q_heads=16, head_dim_qk=64,
                                                     head_dim_v=64)),
@@ -131,8 +138,8 @@ def test_multi_with_one_token_equals_one_token_calls(wl_name, over, lengths):
 
 @pytest.mark.parametrize("wl_name", ["mla-128h", "mla-64h-b512"])
 def test_lazy_max_mla_recomputes_workers_whose_scores_outrun_the_first_tile(wl_name):
-    """128 query rows per unit take the 32-rows-per-wave kernel and 64 rows the wave-pair
-    kernel; both take weights relative to each segment's first-tile maximum. Two keys planted
+    """The wave-pair kernel (8 waves for 128 query rows per unit, 4 for 64) takes weights
+    relative to each segment's first-tile maximum. Two keys planted
     mid-shard score about 90 (natural log units) above the rest, so those workers are
     recomputed by the general kernel: the result still matches the oracle and flag bit 2
     reports the recomputation."""
@@ -165,13 +172,13 @@ def test_lazy_max_mla_recomputes_workers_whose_scores_outrun_the_first_tile(wl_n
     fo, fl = O.full_attention("mla", wl.dtype, hq, caches, bt, lens, bs, wl.softmax_scale,
                               wl.head_dim_v)
     assert float(np.max(fl[0])) > 80.0
-    assert_close(out.cpu().numpy(), out_lse.cpu().numpy(), fo, fl, wl.dtype, "planted wide")
+    assert_close(out.cpu().numpy(), out_lse.cpu().numpy(), fo, fl, wl.dtype, "planted high score")
 
 
 @pytest.mark.parametrize("wl_name,over,lengths,T", [
     ("gqa-g16", dict(batch=2), [300, 200], 4),       # 64 rows per KV head: gqa_chunk_kernel
-    ("mla-64h-b512", dict(batch=2), [300, 200], 2),  # 128 rows: mla_wide_kernel
-    ("mla-128h", dict(batch=2), [300, 200], 1),      # 128 heads: mla_wide_kernel
+    ("mla-64h-b512", dict(batch=2), [300, 200], 2),  # 128 rows: mla_pair_kernel<8>
+    ("mla-128h", dict(batch=2), [300, 200], 1),      # 128 heads: mla_pair_kernel<8>
 ])
 def test_multi_row_kernels_flag_invalid_device_values(wl_name, over, lengths, T):
     """The kernels for many rows per KV tile mask a block id outside the pool and clamp a

@@ -153,13 +153,14 @@ def test_any_partition_merges_to_full_attention(wl_name, over, lengths):
 @pytest.mark.parametrize("wl_name,over,lengths", [
     ("mla-64h-b512", dict(batch=3), [1000, 77, 4097]),                   # wave pairs
     ("mla-64h-b512", dict(batch=2, num_q_heads=32), [900, 61]),         # 16 rows per wave
-    ("mla-128h", dict(batch=2), [2000, 45]),                            # 32 rows per wave
+    ("mla-128h", dict(batch=2), [2000, 45]),                            # 8-wave pairs
     ("mla-64h-b512", dict(batch=2, block_size=16), [500, 77]),         # tiles over 2 pages
     ("mla-64h-b512", dict(batch=2, num_q_heads=32, block_size=16), [300, 50]),
+    ("mla-128h", dict(batch=2, block_size=16), [400, 39]),
     ("gqa-g16", dict(batch=3), [1000, 77, 3001]),                       # MFMA kernel
     ("gqa-g16", dict(batch=2, dtype="f32"), [700, 45]),                 # VALU kernel
-], ids=["mla-64h", "mla-32h", "mla-128h", "mla-64h-bs16", "mla-32h-bs16", "gqa-g16",
-        "gqa-g16-f32"])
+], ids=["mla-64h", "mla-32h", "mla-128h", "mla-64h-bs16", "mla-32h-bs16", "mla-128h-bs16",
+        "gqa-g16", "gqa-g16-f32"])
 def test_unused_slots_past_the_context_stay_out_of_the_output(wl_name, over, lengths):
     """A page's slots past the context end may hold anything in a real cache. Filled with NaN
     here, they must not reach the output: masked tokens get weight 0, and 0 * NaN would
