@@ -606,7 +606,10 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
       const uint32_t mask =
           mask_next & (dl < 0 ? 0u : dl >= kTile - 1 ? 0xFFFFFFFFu : (2u << dl) - 1u);
       const bool more = tile + kTile < t1i;
+      // copies are queued at raised wave priority too (see the value loop)
+      __builtin_amdgcn_s_setprio(1);
       if (more) mask_next = issue_tile(tile + kTile, cur ^ 1, kQ0);
+      __builtin_amdgcn_s_setprio(0);
       const char* tb = &lds[cur * kTileBytes];
 
       // S^T = K . Q^T for the two 16-row subtiles
@@ -638,7 +641,9 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
         __builtin_amdgcn_sched_barrier(0);
       }
 
+      __builtin_amdgcn_s_setprio(1);
       if (more && one) issue_rows(kQ0, kRows);  // the rest of a one-page tile's row copies
+      __builtin_amdgcn_s_setprio(0);
       // weights against the fixed reference; s[at][i] is MFMA row 4gq + i of subtile at. The
       // mask is wave-uniform; a tile with every token visible (all but a segment's edges)
       // skips the per-score masking and the -inf guards.
@@ -720,8 +725,9 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
         const char* v0 = tb + vb + 1024 * s2 + ((32 * (mt ^ s2)) ^ vxq);
         return mla_tr_pair(v0, v0 + 16 * 1024);
       };
-      // the value MFMAs run at raised wave priority: while one wave of a SIMD multiplies, the
-      // other is queueing copies or reading scores (1-1.4% faster per launch than without)
+      // the value MFMAs and the copy issue run at raised wave priority, the scores and the
+      // softmax at the base level: a wave that multiplies or queues copies goes first (about
+      // 1% faster per launch for each of the two)
       __builtin_amdgcn_s_setprio(1);
       constexpr int kVPre = 2;
       bf16x8 vbuf[kVPre];
