@@ -36,13 +36,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
-    "mla": ["k_mla_mfma.hip", "device_common.h", "dcp_internal.h"],
-    "mla-pair": ["k_mla_mfma.hip", "device_common.h", "dcp_internal.h"],
+    "mla": ["k_mla_mfma.hip", "mla_common.h", "device_common.h", "dcp_internal.h"],
+    "mla-ring": ["k_mla_ring.hip", "mla_common.h", "device_common.h", "dcp_internal.h"],
+    "mla-pair": ["k_mla_mfma.hip", "mla_common.h", "device_common.h", "dcp_internal.h"],
     "gqa-mfma": ["k_gqa_mfma.hip", "device_common.h", "dcp_internal.h"],
     "gqa-chunk": ["k_gqa_chunk.hip", "device_common.h", "dcp_internal.h"],
     "gqa-valu": ["k_gqa_valu.hip", "device_common.h", "dcp_internal.h"],
 }
-KERNEL_NAMES = {"mla": "mla_mfma_kernel", "mla-pair": "mla_pair_kernel",
+KERNEL_NAMES = {"mla": "mla_mfma_kernel", "mla-ring": "mla_ring_kernel",
+                "mla-pair": "mla_pair_kernel",
                 "gqa-mfma": "gqa_mfma_kernel", "gqa-chunk": "gqa_chunk_kernel",
                 "gqa-valu": "gqa_valu_kernel"}
 
@@ -76,10 +78,10 @@ def parse_args():
 
 def kernel_family(wl, q_len=1):
     if wl.kind == "mla":
-        # more than 32 query rows per unit take the wave-pair kernel (4 waves for 64 rows, 8
-        # for 128), fewer the 16-rows-per-wave kernel
+        # units of 64 query rows take the 12-wave ring kernel, of 128 the 8-wave pair kernel,
+        # smaller units the 16-rows-per-wave kernel
         rows = q_len * wl.num_q_heads
-        return "mla-pair" if rows > 32 else "mla"
+        return "mla-pair" if rows > 64 else "mla-ring" if rows > 32 else "mla"
     g = wl.num_q_heads // wl.num_kv_heads
     if wl.dtype == "bf16" and g <= 16 and wl.head_dim_qk == 128 and g * q_len > 16:
         return "gqa-chunk"   # more than 16 query rows per KV head share each K/V tile

@@ -22,6 +22,7 @@ SOURCES = [
     ("k_gqa_mfma.hip", "k_gqa_mfma", []),
     ("k_gqa_chunk.hip", "k_gqa_chunk", []),
     ("k_mla_mfma.hip", "k_mla_mfma", []),
+    ("k_mla_ring.hip", "k_mla_ring", []),
 ]
 
 # -packed-fp32-ops keeps hipcc from emitting packed fp32 VALU ops (v_pk_*_f32).

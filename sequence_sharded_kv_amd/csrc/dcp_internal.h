@@ -123,5 +123,6 @@ int32_t gqa_chunk_workers(int device, int32_t Ru, int32_t max_workers);
 hipError_t launch_gqa_chunk(const AttnArgs& a, hipStream_t stream);
 int32_t mla_mfma_workers(int device, int32_t Ru, int32_t max_workers);
 hipError_t launch_mla_mfma(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_mla_ring(const AttnArgs& a, hipStream_t stream);  // 64 rows per unit
 
 }  // namespace dcp

@@ -20,49 +20,15 @@
 // pi(8c + 4h + e) = 8c + h + 2e: the K reads of 8 consecutive MFMA rows then touch 8
 // different 16-byte bank groups, and each transposed V read (4 MFMA rows e = 0..3) reads
 // rows 2 apart, whose 32-byte pieces tile 128 bytes of banks without overlap.
-#include "device_common.h"
+#include "mla_common.h"
 
 namespace dcp {
 
-constexpr int kMlaDqk = 576;
-constexpr int kMlaDv = 512;
 constexpr int kMlaTile = 32;
 constexpr int kMlaRowA = 1056;                    // LDS bytes per row, region A (dims 0..511)
 constexpr int kMlaRowB = 128;                     // LDS bytes per row, region B (dims 512..575)
 constexpr int kMlaRegionB = kMlaTile * kMlaRowA;  // offset of region B
 constexpr int kMlaTileBytes = kMlaRegionB + kMlaTile * kMlaRowB;
-
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Token (within a 16-row subtile) held by MFMA row m (see the layout note above).
-__device__ __forceinline__ int tok_of_row(int m) {
-  return (m & 8) | ((m >> 2) & 1) | ((m & 3) << 1);
-}
-__device__ __forceinline__ int swz_b(int r) { return r & 7; }
-
-__device__ __forceinline__ bf16x8 mla_tr_pair(const char* lo, const char* hi) {
-  i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)lo);
-  i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)hi);
-  typedef __attribute__((ext_vector_type(8))) short i16x8;
-  i16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-  return __builtin_bit_cast(bf16x8, z);
-}
-
-// max / sum over the four lanes n, n+16, n+32, n+48 that hold one head, with the VALU lane
-// swaps of gfx950 (cross-lane LDS operations would queue behind the tile reads)
-__device__ __forceinline__ float quad_max(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float quad_sum(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
 
 template <int NW>  // waves per workgroup; 16 heads per wave, Hq = 16 * NW
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -377,25 +343,6 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row, const int32_t* __
 // conflicted in half of the wave (SQ_LDS_BANK_CONFLICT 3.2e8 cycles per launch against 6.4e8
 // for c ^ (r & 15)). A fully conflict-free mapping (32 consecutive dims per block, groups 16
 // dims apart) measured 2.5% slower in the same runs, for reasons the counters do not show.
-// One 16-byte-per-lane HBM -> LDS copy from a wave-uniform 64-bit base in scalar registers
-// plus a 32-bit per-lane byte offset (the SADDR form of global_load_lds_dwordx4): one VALU
-// operation per copy for the offset instead of a 64-bit address per lane. Lane i's 16 bytes
-// land at lds_addr + 16 i. The non-temporal policy, the M0 handling and the explicit waits are
-// as for dma16.
-__device__ __forceinline__ void dma16s(uint64_t sbase, uint32_t voff, uint32_t lds_addr) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);  // wave-uniform by contract
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2 nt\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(sbase), "s"(m0v)
-      : "memory");
-}
-
 namespace pair {
 constexpr int kTile = 32;
 constexpr int kRegionB = 32 * 1024;
@@ -409,7 +356,7 @@ struct Cfg {
 constexpr float kLazy = 64.f;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 // region-A chunk swizzle: bits 1-4 from the row's low four bits, bit 5 from its bit 3
-__device__ __forceinline__ int swz_a(int r) { return (2 * (r & 15)) ^ (32 * ((r >> 3) & 1)); }
+__device__ __forceinline__ int swz_a(int r) { return mla_swz_a(r); }
 }  // namespace pair
 
 template <int NW>  // 4 waves for 64 rows per unit (two workgroups per CU), 8 for 128 (one)
@@ -797,19 +744,12 @@ mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
   }
 }
 
-static int mla_cus(int device) {
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
-  return cus;
-}
-
 int32_t mla_mfma_workers(int device, int32_t Ru, int32_t max_workers) {
-  // LDS (2 x 36.5 KB per workgroup) allows two resident workgroups per CU; registers allow
-  // two waves per SIMD, so two workgroups fit while a workgroup has at most four waves.
+  // 64 rows: one 12-wave ring workgroup per CU (156 KB of LDS). Otherwise LDS (2 x 36.5 KB per
+  // workgroup) allows two resident workgroups per CU and registers two waves per SIMD, so two
+  // workgroups fit while a workgroup has at most four waves.
   const int nw = Ru / 16;
-  const int per_cu = nw <= 4 ? 2 : 1;
+  const int per_cu = (Ru == 64 || nw > 4) ? 1 : 2;
   int32_t p = mla_cus(device) * per_cu;
   return p < max_workers ? p : max_workers;
 }
@@ -820,7 +760,8 @@ hipError_t launch_mla_mfma(const AttnArgs& a, hipStream_t stream) {
     // pairs of waves share the value product; workers whose scores outran the fixed
     // reference are recomputed by the 16-rows-per-wave kernel (same worker count)
     if (a.Ru == 64) {
-      hipLaunchKernelGGL((mla_pair_kernel<4>), dim3(a.P), dim3(256), 0, stream, a, zr, a.redo);
+      const hipError_t e = launch_mla_ring(a, stream);
+      if (e != hipSuccess) return e;
       hipLaunchKernelGGL((mla_mfma_kernel<4>), dim3(a.P), dim3(256), 0, stream, a, zr,
                          (const int32_t*)a.redo);
     } else {

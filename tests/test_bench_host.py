@@ -57,10 +57,10 @@ def test_flop_model_is_the_causal_sum(bench):
 
 
 def test_kernel_family_follows_the_row_count(bench):
-    assert bench.kernel_family(workload("mla-64h-b512"), 1) == "mla-pair"   # 64 rows
+    assert bench.kernel_family(workload("mla-64h-b512"), 1) == "mla-ring"   # 64 rows, 12 waves
     assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=32), 1) == "mla"
-    assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=32), 2) == "mla-pair"
-    assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=16), 3) == "mla-pair"
+    assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=32), 2) == "mla-ring"
+    assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=16), 3) == "mla-ring"
     assert bench.kernel_family(workload("mla-64h-b512"), 2) == "mla-pair"   # 128 rows, 8 waves
     assert bench.kernel_family(workload("mla-128h"), 1) == "mla-pair"
     assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=16), 5) == "mla-pair"

@@ -177,6 +177,7 @@ def test_lazy_max_mla_recomputes_workers_whose_scores_outrun_the_first_tile(wl_n
 
 @pytest.mark.parametrize("wl_name,over,lengths,T", [
     ("gqa-g16", dict(batch=2), [300, 200], 4),       # 64 rows per KV head: gqa_chunk_kernel
+    ("mla-64h-b512", dict(batch=2), [300, 200], 1),  # 64 rows: mla_ring_kernel
     ("mla-64h-b512", dict(batch=2), [300, 200], 2),  # 128 rows: mla_pair_kernel<8>
     ("mla-128h", dict(batch=2), [300, 200], 1),      # 128 heads: mla_pair_kernel<8>
 ])
