@@ -34,6 +34,9 @@
  *    memory and keeps no state beyond a per-device cache of launch
  *    parameters, the thread-local error string and, between
  *    dcp_kernel_timing_begin and _end, the calling thread's timing events.
+ *    The one exception is the static device scratch of
+ *    dcp_decode_attn_noalloc (DCP_NOALLOC_SCRATCH_BYTES per GPU, part of the
+ *    loaded module and held until the process ends).
  *  - Device pointers to Q, caches, partials, outputs and workspace must be
  *    16-byte aligned (the kernels use 128-bit loads and stores).
  *  - Values that only exist on the device (bounds, block-table entries) are
@@ -178,6 +181,27 @@ dcp_status dcp_decode_attn(const dcp_attn_shape* shape, const void* q, const voi
                            const void* v_cache, const int32_t* block_table, const int32_t* bounds,
                            void* workspace, size_t workspace_bytes, float* out, float* out_lse,
                            void* stream);
+
+/*
+ * dcp_decode_attn_noalloc -- dcp_decode_attn for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * workspace is a device array inside the library, DCP_NOALLOC_SCRATCH_BYTES (256 MiB) per GPU,
+ * one copy on each GPU the library runs on, kept until the process ends. Arguments, results
+ * and errors are those of dcp_decode_attn without the workspace pair. The call allocates
+ * nothing: no hipMalloc, hipFree or allocating library routine (the first call on a device
+ * looks up that device's copy of the array once). Every call on one GPU shares that GPU's
+ * scratch, which keeps the last call's contents; each call rewrites all it reads before
+ * reading it, so no clearing is needed, but calls that overlap on one GPU (on different
+ * streams, or from several threads without ordering) race on it and give undefined results.
+ * Errors additionally: DCP_ERR_WORKSPACE, before any device work, when the shape needs more
+ * than DCP_NOALLOC_SCRATCH_BYTES of workspace (dcp_workspace_bytes); DCP_ERR_DEVICE when the
+ * current device index is 64 or above.
+ */
+#define DCP_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+dcp_status dcp_decode_attn_noalloc(const dcp_attn_shape* shape, const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, const int32_t* bounds, float* out,
+                                   float* out_lse, void* stream);
 
 /*
  * Several query tokens per request: speculative decoding / MTP verification (2 .. 16 tokens)

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     DCP_F32,
     DCP_KV_GQA,
     DCP_KV_MLA,
+    DCP_NOALLOC_SCRATCH_BYTES,
     DCP_OK,
     EXPORTS,
     LIB_PATH,
@@ -28,6 +29,7 @@ from ._lib import (  # noqa: F401
     dcp_decode_attn,
     dcp_decode_attn_multi,
     dcp_decode_attn_multi_partial,
+    dcp_decode_attn_noalloc,
     dcp_decode_attn_partial,
     dcp_kernel_timing_begin,
     dcp_kernel_timing_end,

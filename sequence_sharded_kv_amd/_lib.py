@@ -36,7 +36,11 @@ EXPORTS = (
     "dcp_decode_attn", "dcp_read_device_flags", "dcp_debug_gather_shard",
     "dcp_kernel_timing_begin", "dcp_kernel_timing_end", "dcp_append_kv",
     "dcp_workspace_bytes_multi", "dcp_decode_attn_multi_partial", "dcp_decode_attn_multi",
+    "dcp_decode_attn_noalloc",
 )
+
+# device scratch of dcp_decode_attn_noalloc (DCP_NOALLOC_SCRATCH_BYTES)
+DCP_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class DcpError(RuntimeError):
@@ -88,6 +92,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "dcp_workspace_bytes_multi": (I32, [SH, I32, ctypes.POINTER(SZ)]),
         "dcp_decode_attn_multi_partial": (I32, [SH, I32, P, P, P, P, P, P, P, P, SZ, P]),
         "dcp_decode_attn_multi": (I32, [SH, I32, P, P, P, P, P, P, SZ, P, P, P]),
+        "dcp_decode_attn_noalloc": (I32, [SH, P, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -184,6 +189,13 @@ def dcp_decode_attn(shape: dcp_attn_shape, q, k_cache, v_cache, block_table, bou
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(bounds), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
         _ptr(out_lse), _stream(q)))
+
+
+def dcp_decode_attn_noalloc(shape: dcp_attn_shape, q, k_cache, v_cache, block_table, bounds,
+                            out, out_lse=None) -> None:
+    _check(load().dcp_decode_attn_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(bounds), _ptr(out), _ptr(out_lse), _stream(q)))
 
 
 def dcp_workspace_bytes_multi(shape: dcp_attn_shape, q_len: int) -> int:

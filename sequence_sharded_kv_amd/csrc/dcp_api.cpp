@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -52,6 +53,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace of dcp_decode_attn_noalloc: a file-scope device array, one copy per GPU, held
+// from the module's load until the process ends. Its name is a host-side stand-in; kernels
+// get the device address that hipGetSymbolAddress returns, looked up once per device.
+static __device__ __align__(256) char scratch[DCP_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
 
 // Upper bounds on workers (stream-K ranges) per kernel family; the launch uses at most this.
 constexpr int32_t kMaxWorkersWave = 4096;  // GQA kernels: one wave per worker
@@ -131,7 +140,8 @@ dcp_status make_plan(const dcp_attn_shape* sh, int32_t Tq, dcp::Plan* plan) {
     // waves of 16 rows, a power of two of them up to 8 per workgroup
     ru = 16;
     while (ru < rows && ru < 128) ru *= 2;
-    pmax = kMaxWorkersMla;
+    // units of 64 or 128 rows run one workgroup per CU (256 on gfx950), smaller ones two
+    pmax = ru >= 64 ? kMaxWorkersMla / 2 : kMaxWorkersMla;
   }
   const int32_t groups = (rows + ru - 1) / ru;
   const int64_t units64 = (int64_t)sh->batch * sh->num_shards *
@@ -400,6 +410,45 @@ dcp_status dcp_decode_attn(const dcp_attn_shape* shape, const void* q, const voi
                            void* stream) {
   return dcp_decode_attn_multi(shape, 1, q, k_cache, v_cache, block_table, bounds, workspace,
                                workspace_bytes, out, out_lse, stream);
+}
+
+dcp_status dcp_decode_attn_noalloc(const dcp_attn_shape* shape, const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, const int32_t* bounds, float* out,
+                                   float* out_lse, void* stream) {
+  dcp::Plan plan;
+  dcp_status st = make_plan(shape, 1, &plan);
+  if (st != DCP_OK) return st;
+  if (!q || !k_cache || !block_table || !bounds || !out)
+    return fail(DCP_ERR_NULL, "q, k_cache, block_table, bounds and out must be non-NULL");
+  if (plan.ws.total > DCP_NOALLOC_SCRATCH_BYTES)
+    return fail(DCP_ERR_WORKSPACE,
+                "this shape needs %zu bytes of workspace; the static scratch of "
+                "dcp_decode_attn_noalloc holds %zu (use dcp_decode_attn with a workspace)",
+                plan.ws.total, (size_t)DCP_NOALLOC_SCRATCH_BYTES);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(DCP_ERR_DEVICE, "device %d: the static scratch is tracked for devices 0..%d",
+                dev, kMaxScratchDevices - 1);
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      // first call on this device (the current one): its copy of the array
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return device_fail(e, "hipGetSymbolAddress(scratch)");
+      if (!p) return fail(DCP_ERR_DEVICE, "hipGetSymbolAddress(scratch) returned NULL");
+      g_scratch_ptr[dev] = p;
+    }
+    ws = g_scratch_ptr[dev];
+  }
+  // every word the kernels read is written earlier in the same call (the schedule kernel
+  // clears the flags, the zero row and the recomputation marks), so nothing is cleared here
+  return dcp_decode_attn(shape, q, k_cache, v_cache, block_table, bounds, ws,
+                         DCP_NOALLOC_SCRATCH_BYTES, out, out_lse, stream);
 }
 
 dcp_status dcp_read_device_flags(const void* workspace, int32_t* flags, void* stream) {

@@ -24,7 +24,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = dcp.load()
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(dcp.EXPORTS) == names
@@ -156,6 +156,31 @@ def test_merge_and_fused_error_paths():
     assert lib.dcp_read_device_flags(None, None, None) == dcp.DCP_ERR_NULL
     assert lib.dcp_kernel_timing_begin(0) == dcp.DCP_ERR_SHAPE
     assert lib.dcp_kernel_timing_end(None, None) == dcp.DCP_ERR_NULL
+
+
+def test_noalloc_limit_and_error_paths_return_before_device_work():
+    """The no-allocation entry point states its scratch size in the header and refuses a
+    shape whose workspace exceeds it before touching the device."""
+    text = open(HEADER).read()
+    m = re.search(r"#define DCP_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == dcp.DCP_NOALLOC_SCRATCH_BYTES
+    lib = dcp.load()
+    A = 0x10000
+    big = _shape(batch=512, num_shards=8)  # 64 heads x 512 dims x 4096 shards of partials
+    assert dcp.dcp_workspace_bytes(big) > dcp.DCP_NOALLOC_SCRATCH_BYTES
+    assert lib.dcp_decode_attn_noalloc(ctypes.byref(big), A, A, None, A, A, A, None, None) == \
+        dcp.DCP_ERR_WORKSPACE
+    assert "static scratch" in dcp.dcp_last_error()
+    small = _shape()
+    assert dcp.dcp_workspace_bytes(small) <= dcp.DCP_NOALLOC_SCRATCH_BYTES
+    assert lib.dcp_decode_attn_noalloc(ctypes.byref(small), None, A, None, A, A, A, None,
+                                       None) == dcp.DCP_ERR_NULL
+    assert lib.dcp_decode_attn_noalloc(ctypes.byref(small), A, A, None, A, A, None, None,
+                                       None) == dcp.DCP_ERR_NULL
+    assert lib.dcp_decode_attn_noalloc(None, A, A, None, A, A, A, None, None) == dcp.DCP_ERR_NULL
+    bad = _shape(num_shards=0)
+    assert lib.dcp_decode_attn_noalloc(ctypes.byref(bad), A, A, None, A, A, A, None, None) == \
+        dcp.DCP_ERR_SHAPE
 
 
 def test_append_error_paths_return_before_device_work():
