@@ -59,6 +59,9 @@ def parse_args():
                    help="query tokens per request (speculative / MTP decode); 1 = plain decode")
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--ceiling-gib", type=float, default=4.0,
+                   help="buffer size of the HBM streaming-read ceiling measured in the same run "
+                        "(0 skips it)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--calibration-copy-gib", type=float, default=0.0,
@@ -210,7 +213,61 @@ def summarize_mfma(d, workload, family, wl):
     return out
 
 
+# ------------------------------------------------------------------ HBM read ceiling
+
+def hbm_read_ceiling(dev, gib, launches=10):
+    """Read rate of a plain streaming kernel (dcp_hbm_read_ceiling: 128-bit non-temporal loads
+    over every CU) on a `gib` GiB buffer, timed with HIP events on the stream it runs on."""
+    import torch
+    import sequence_sharded_kv_amd as dcp
+    n = int(gib * (1 << 30)) // 16 * 16
+    buf = torch.zeros(n, dtype=torch.uint8, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(2 * cus, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        dcp.dcp_hbm_read_ceiling(buf, sink)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(launches):
+        dcp.dcp_hbm_read_ceiling(buf, sink)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / launches
+    del buf, sink
+    gbs = n / (ms * 1e-3) / 1e9
+    return {"GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": n, "launches": launches, "ms_per_launch": round(ms, 4),
+            "kernel": "stream_read_kernel"}
+
+
 # ------------------------------------------------------------------ CPU baseline
+
+def host_info():
+    """CPU model, logical CPUs visible to this process and RAM of the host."""
+    model, ram = None, None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal"):
+                    ram = round(int(line.split()[1]) / (1 << 20), 1)
+                    break
+    except OSError:
+        pass
+    try:
+        visible = len(os.sched_getaffinity(0))
+    except OSError:
+        visible = os.cpu_count()
+    return {"cpu_model": model, "logical_cpus_visible": visible, "ram_gib": ram}
+
 
 def cpu_baseline(wl, inp, bounds_np, seconds):
     """The float64 oracle, as it stands, on whole sequences drawn in a seeded order until
@@ -252,7 +309,7 @@ def cpu_baseline(wl, inp, bounds_np, seconds):
             break
     sample = byte_model(wl.replace(batch=len(done)), lens[done])
     return {"value": sample["step"] / elapsed / 1e12, "unit": "TB/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", **host_info(),
             "sample": f"{len(done)} of {wl.batch} requests ({sample['tokens']} tokens, all "
                       f"{wl.num_shards} shards + merge), float64 numpy, {elapsed:.1f} s"}
 
@@ -423,6 +480,11 @@ def main():
                     "kernel": KERNEL_NAMES[family], "kernel_avg_ms": round(kern_avg_ms, 4),
                     "algorithmic_flops_per_launch": int(flops)}
     append = time_append(wl, sh, inp, k_cache, v_cache, dev, 200, step)
+    ceiling = None
+    if args.ceiling_gib > 0:
+        ceiling = hbm_read_ceiling(dev, args.ceiling_gib)
+        if roofline["unit"] == "GB/s":
+            roofline["frac_of_read_ceiling"] = round(roofline["achieved"] / ceiling["GBps"], 4)
     cpu = None
     if not args.no_cpu_baseline and T == 1:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -454,6 +516,7 @@ def main():
                    "parallelism": "all shards on one GPU"},
         "roofline": roofline,
         "mfma": mfma,
+        "hbm_read_ceiling": ceiling,
         "cpu_baseline": cpu,
         "append_kv": append,
     }

@@ -295,6 +295,17 @@ dcp_status dcp_append_kv(const dcp_attn_shape* shape, const int32_t* seq_lens, c
                          void* v_cache, int32_t* owner, void* stream);
 
 /*
+ * dcp_hbm_read_ceiling -- measurement aid, not part of the attention path: read `bytes` (a
+ * positive multiple of 16) of the device buffer `src` (16-byte aligned) once with 128-bit
+ * non-temporal loads spread over every CU, and write one word per workgroup to `sink`
+ * (device int32, at least 2 x the CU count entries; the values are meaningless). Timing a few
+ * launches over a buffer of some GiB gives the HBM read rate that a plain streaming kernel
+ * reaches on this device, which bench.py reports beside the 8 TB/s peak. Errors: DCP_ERR_NULL,
+ * DCP_ERR_ALIGN, DCP_ERR_SHAPE, DCP_ERR_DEVICE.
+ */
+dcp_status dcp_hbm_read_ceiling(const void* src, size_t bytes, int32_t* sink, void* stream);
+
+/*
  * Kernel timing for benchmarks (no effect on results). dcp_kernel_timing_begin(n) creates n
  * pairs of HIP events; while timing is on for the calling thread, each of the next n
  * dcp_decode_attn / dcp_decode_attn_partial calls records one pair around its

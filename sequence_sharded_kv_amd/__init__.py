@@ -31,6 +31,7 @@ from ._lib import (  # noqa: F401
     dcp_decode_attn_multi_partial,
     dcp_decode_attn_noalloc,
     dcp_decode_attn_partial,
+    dcp_hbm_read_ceiling,
     dcp_kernel_timing_begin,
     dcp_kernel_timing_end,
     dcp_last_error,

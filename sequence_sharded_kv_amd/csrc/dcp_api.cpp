@@ -500,6 +500,23 @@ dcp_status dcp_append_kv(const dcp_attn_shape* shape, const int32_t* seq_lens,
   return ok();
 }
 
+dcp_status dcp_hbm_read_ceiling(const void* src, size_t bytes, int32_t* sink, void* stream) {
+  if (!src || !sink) return fail(DCP_ERR_NULL, "src and sink must be non-NULL");
+  if (!aligned16(src)) return fail(DCP_ERR_ALIGN, "src must be 16-byte aligned");
+  if (bytes == 0 || bytes % 16 != 0)
+    return fail(DCP_ERR_SHAPE, "bytes (%zu) must be a positive multiple of 16", bytes);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return device_fail(e, "hipDeviceGetAttribute");
+  // two workgroups of 8 waves per CU
+  e = dcp::launch_stream_read(src, bytes, sink, 2 * (cus > 0 ? cus : 256), as_stream(stream));
+  if (e != hipSuccess) return device_fail(e, "stream-read launch");
+  return ok();
+}
+
 dcp_status dcp_kernel_timing_begin(int32_t max_launches) {
   if (max_launches < 1) return fail(DCP_ERR_SHAPE, "max_launches must be >= 1");
   destroy_timing_events();

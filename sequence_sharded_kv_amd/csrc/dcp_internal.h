@@ -124,5 +124,7 @@ hipError_t launch_gqa_chunk(const AttnArgs& a, hipStream_t stream);
 int32_t mla_mfma_workers(int device, int32_t Ru, int32_t max_workers);
 hipError_t launch_mla_mfma(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_mla_ring(const AttnArgs& a, hipStream_t stream);  // 64 rows per unit
+hipError_t launch_stream_read(const void* src, size_t bytes, int32_t* sink, int32_t blocks,
+                              hipStream_t stream);
 
 }  // namespace dcp

@@ -429,4 +429,39 @@ hipError_t launch_append_kv(const dcp_attn_shape& sh, const int32_t* seq_lens,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- HBM read ceiling
+
+// Measurement aid, not part of the attention path: stream a buffer with 128-bit non-temporal
+// loads and fold the words so that the loads stay live. A workgroup reads 64 KB of
+// consecutive bytes per iteration (eight 1 KB loads per wave, all in flight at once), and
+// the workgroups take the 64 KB chunks in turn.
+constexpr int kStreamThreads = 512;
+constexpr int64_t kStreamChunk16 = 8 * kStreamThreads;  // 16-byte words per chunk (64 KB)
+
+__global__ void __launch_bounds__(kStreamThreads)
+stream_read_kernel(const u32x4* __restrict__ src, int64_t n16, int32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint32_t acc = 0;
+  for (int64_t c = (int64_t)blockIdx.x * kStreamChunk16; c < n16;
+       c += (int64_t)gridDim.x * kStreamChunk16) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t i = c + 64 * (8 * k + wv) + lane;  // 1 KB block 8 k + wv of the chunk
+      v[k] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
+  }
+  // one word per workgroup (lane 0 of wave 0), so the result is used
+  if (threadIdx.x == 0) sink[blockIdx.x] = (int32_t)acc;
+}
+
+hipError_t launch_stream_read(const void* src, size_t bytes, int32_t* sink, int32_t blocks,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(kStreamThreads), 0, stream,
+                     (const u32x4*)src, (int64_t)(bytes / 16), sink);
+  return hipGetLastError();
+}
+
 }  // namespace dcp

@@ -11,6 +11,21 @@ import pytest
 import sequence_sharded_kv_amd as dcp
 from oracle import plan_shards as oracle_plan
 
+def _gpu_visible():
+    """Counting devices does not initialise the GPU."""
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:  # noqa: BLE001
+        return False
+
+
+# These tests pass fabricated device addresses into entry points that launch kernels once
+# validation passes; every call is built to fail validation first. On a host with a GPU a
+# reordered check could launch on a bogus address, so they run only where no GPU is visible.
+fake_addresses = pytest.mark.skipif(
+    _gpu_visible(), reason="fabricated device addresses: run on a host without a GPU")
+
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
                       "dcp.h")
 
@@ -23,8 +38,10 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     lib = dcp.load()
+    # DCP_LIBRARY selects another build of the library (the sanitized one)
+    assert lib._name == (os.environ.get("DCP_LIBRARY") or dcp.LIB_PATH)
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(dcp.EXPORTS) == names
@@ -124,6 +141,7 @@ def _call_partial(sh, q, k, v, bt, bounds, po, pl, ws):
                                        p(po), p(pl), p(ws), ws.nbytes if ws else 0, None)
 
 
+@fake_addresses
 def test_partial_error_paths_return_before_device_work():
     sh = _shape()
     need = dcp.dcp_workspace_bytes(sh)
@@ -140,6 +158,7 @@ def test_partial_error_paths_return_before_device_work():
     assert "v_cache" in dcp.dcp_last_error()
 
 
+@fake_addresses
 def test_merge_and_fused_error_paths():
     lib = dcp.load()
     assert lib.dcp_merge_lse(2, 4, 8, 64, None, 0x1000, 0x2000, None, None) == dcp.DCP_ERR_NULL
@@ -158,6 +177,7 @@ def test_merge_and_fused_error_paths():
     assert lib.dcp_kernel_timing_end(None, None) == dcp.DCP_ERR_NULL
 
 
+@fake_addresses
 def test_noalloc_limit_and_error_paths_return_before_device_work():
     """The no-allocation entry point states its scratch size in the header and refuses a
     shape whose workspace exceeds it before touching the device."""
@@ -183,6 +203,7 @@ def test_noalloc_limit_and_error_paths_return_before_device_work():
         dcp.DCP_ERR_SHAPE
 
 
+@fake_addresses
 def test_append_error_paths_return_before_device_work():
     lib = dcp.load()
     A = 0x10000
@@ -211,6 +232,7 @@ def test_append_error_paths_return_before_device_work():
     assert call(gqa_odd, nv=A, vc=A) == dcp.DCP_ERR_UNSUPPORTED
 
 
+@fake_addresses
 def test_multi_token_shapes_and_errors():
     sh = _shape()
     one = dcp.dcp_workspace_bytes(sh)
