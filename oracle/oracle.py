@@ -238,14 +238,15 @@ def sharded_attention(kind, dtype, q, caches, block_table, seq_lens, num_shards,
 # ---------------------------------------------------------------- several query tokens
 
 def partial_attention_multi(kind: str, dtype: str, q, caches, block_table, bounds,
-                            block_size: int, scale: float, head_dim_v: int, seqs=None):
+                            block_size: int, scale: float, head_dim_v: int, seqs=None,
+                            tokens=None):
     """Per-shard partials for q_len query tokens per request, with causal visibility.
 
     q [B, q_len, Hq, Dqk]; bounds [B, S, 2]. With L_b the largest end among request b's
     ranges, query token j sits at position L_b - q_len + j and sees token t only when
     t <= L_b - q_len + j. Returns part_o [B, S, q_len, Hq, Dv] and part_lse [B, S, q_len, Hq]
     (a row that sees nothing in a shard gets O = 0, LSE = -inf; rows of sequences not in
-    `seqs` stay NaN).
+    `seqs`, and query tokens j not in `tokens` when it is given, stay NaN).
     """
     B, q_len, Hq = q.shape[0], q.shape[1], q.shape[2]
     S = bounds.shape[1]
@@ -255,7 +256,7 @@ def partial_attention_multi(kind: str, dtype: str, q, caches, block_table, bound
         L = int(np.max(bounds[b, :, 1])) if S else 0
         for s in range(S):
             start, end = int(bounds[b, s, 0]), int(bounds[b, s, 1])
-            for j in range(q_len):
+            for j in (range(q_len) if tokens is None else tokens):
                 last = min(end, L - q_len + j + 1)   # exclusive end of the visible part
                 stop = max(start, last)
                 if kind == "mla":

@@ -376,6 +376,16 @@ def check_multi_rows_are_prefix_decodes():
                                   wl.head_dim_v)
         assert np.allclose(one[0][:, :, 0], ref[0], rtol=1e-13, atol=1e-14)
         assert np.array_equal(np.isneginf(one[1][:, :, 0]), np.isneginf(ref[1]))
+        # a selection of query tokens computes exactly those rows and leaves the rest NaN
+        bounds = O.plan_shards(lens, S, wl.block_size)
+        full = O.partial_attention_multi("gqa", "f32", q, caches, inp["block_table"], bounds,
+                                         wl.block_size, 0.2, wl.head_dim_v)
+        pick = [0, T - 1]
+        sub = O.partial_attention_multi("gqa", "f32", q, caches, inp["block_table"], bounds,
+                                        wl.block_size, 0.2, wl.head_dim_v, tokens=pick)
+        for a, b in zip(sub, full):
+            assert np.array_equal(a[:, :, pick], b[:, :, pick])
+            assert np.isnan(a[:, :, 1:T - 1]).all()
 
 
 def check_multi_brute():

@@ -1,6 +1,10 @@
-"""GPU parity at the full workload sizes, in the launch configuration the benchmark times:
-sampled sequences (shortest, longest and random ones) are checked element by element
-against the float64 oracle; properties that hold at any size are checked on every output."""
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times.
+The three GQA workloads (the 2-request tiny step, the 32-request MoE-shaped layer and the
+4-request 200K-1M stress with planted keys) are compared with the float64 oracle in full:
+every request, shard and head. The two MLA workloads (64 requests x 128 heads, and the
+512-request headline) are compared on every shard and head of 8 seeded requests, the
+shortest and the longest among them; properties that hold at any size are checked on every
+output."""
 
 import numpy as np
 import pytest
@@ -15,9 +19,7 @@ from workloads import make_device_inputs, workload
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
 
-@pytest.mark.parametrize("name,nrand", [("gqa-g16", 2), ("gqa-long", 0), ("mla-128h", 1),
-                                        ("mla-64h-b512", 1)])
-def test_full_size_sampled_parity(name, nrand):
+def _run(name):
     wl = workload(name)
     say(f"[gpu] full-size {name}: drawing inputs")
     inp = make_device_inputs(wl, "cuda")
@@ -34,16 +36,42 @@ def test_full_size_sampled_parity(name, nrand):
     vals = inp["kv_cache"][..., : wl.head_dim_v] if wl.kind == "mla" else inp["v_cache"]
     vmax = max(abs(float(vals.amax().float())), abs(float(vals.amin().float())))
     assert float(out.abs().amax()) <= vmax * (1 + 1e-6)
-    rng = np.random.default_rng(99)
-    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens))}
-                  | set(int(x) for x in rng.choice(wl.batch, size=nrand, replace=False)))
-    say(f"[gpu] full-size {name}: oracle on sequences {seqs} (lengths {[int(lens[s]) for s in seqs]})")
+    return wl, inp, lens, bounds_np, out, out_lse, po, pl
+
+
+def _compare(name, wl, inp, bounds_np, out, out_lse, po, pl, seqs):
     host = host_inputs_of(wl, inp, seqs)
     ro, rl = oracle_partials(wl, host, bounds_np, seqs)
-    mo, ml = O.merge_lse(ro[seqs], rl[seqs])
-    assert_close(po.cpu().numpy()[seqs], pl.cpu().numpy()[seqs], ro[seqs], rl[seqs], wl.dtype,
+    sel = list(range(wl.batch)) if seqs is None else seqs
+    mo, ml = O.merge_lse(ro[sel], rl[sel])
+    assert_close(po.cpu().numpy()[sel], pl.cpu().numpy()[sel], ro[sel], rl[sel], wl.dtype,
                  f"{name} partials")
-    assert_close(out.cpu().numpy()[seqs], out_lse.cpu().numpy()[seqs], mo, ml, wl.dtype,
+    assert_close(out.cpu().numpy()[sel], out_lse.cpu().numpy()[sel], mo, ml, wl.dtype,
                  f"{name} fused")
-    del inp, out, po, pl, ws
+
+
+@pytest.mark.parametrize("name", ["gqa-tiny", "gqa-g16", "gqa-long"])
+def test_full_size_parity_every_request(name):
+    wl, inp, lens, bounds_np, out, out_lse, po, pl = _run(name)
+    say(f"[gpu] full-size {name}: oracle on all {wl.batch} requests "
+        f"(lengths {int(lens.min())}..{int(lens.max())})")
+    _compare(name, wl, inp, bounds_np, out, out_lse, po, pl, None)
+    del inp, out, po, pl
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["mla-128h", "mla-64h-b512"])
+def test_full_size_parity_eight_requests(name):
+    wl, inp, lens, bounds_np, out, out_lse, po, pl = _run(name)
+    rng = np.random.default_rng(99)
+    seqs = {int(np.argmin(lens)), int(np.argmax(lens))}
+    for x in rng.permutation(wl.batch):
+        if len(seqs) == 8:
+            break
+        seqs.add(int(x))
+    seqs = sorted(seqs)
+    say(f"[gpu] full-size {name}: oracle on requests {seqs} "
+        f"(lengths {[int(lens[s]) for s in seqs]})")
+    _compare(name, wl, inp, bounds_np, out, out_lse, po, pl, seqs)
+    del inp, out, po, pl
     torch.cuda.empty_cache()

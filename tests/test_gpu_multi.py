@@ -111,6 +111,64 @@ def test_multi_token_partials_and_fused_match_oracle(name, wl_name, lengths, T, 
                 assert torch.all(out[b, j] == 0) and torch.all(torch.isneginf(out_lse[b, j]))
 
 
+# prefill chunks of the sizes bench.py --q-len times (512 and 4096 tokens) on short contexts:
+# name, workload, lengths, q_len, overrides
+CHUNKS = [
+    ("mla-64h-chunk512", "mla-64h-b512", [1100, 700], 512, dict(batch=2)),
+    ("mla-64h-chunk4096", "mla-64h-b512", [4500], 4096, dict(batch=1, num_shards=4)),
+    ("gqa-g16-chunk512", "gqa-g16", [1300, 600], 512, dict(batch=2)),
+    ("gqa-g16-chunk4096", "gqa-g16", [4400], 4096, dict(batch=1)),
+]
+
+
+@pytest.mark.parametrize("name,wl_name,lengths,T,over", CHUNKS, ids=[c[0] for c in CHUNKS])
+def test_prefill_chunk_sampled_tokens_match_oracle(name, wl_name, lengths, T, over):
+    """Every shard and head of 16 query tokens of the chunk (the first two, the middle, the
+    last two and 11 seeded others), partials and the fused call, against the oracle computed
+    for those tokens alone; every output is finite."""
+    say(f"[gpu] prefill chunk {name} (q_len {T})")
+    wl = workload(wl_name).replace(**over)
+    if wl.length_law == "fixed":
+        wl = wl.replace(lengths=tuple(lengths))
+    host = make_host_inputs(wl, lengths=lengths)
+    inp = to_device(wl, host)
+    qh = make_queries(wl, T)
+    q = _q_device(wl, qh)
+    sh = shape_of(wl, inp)
+    B, S, Hq, Dv = wl.batch, wl.num_shards, wl.num_q_heads, wl.head_dim_v
+    bounds_np = dcp.dcp_plan_shards(host["seq_lens"], S, wl.block_size)
+    bounds = torch.from_numpy(bounds_np).cuda()
+    ws = dcp.alloc_workspace(sh, "cuda", T)
+    k = inp["kv_cache"] if wl.kind == "mla" else inp["k_cache"]
+    v = None if wl.kind == "mla" else inp["v_cache"]
+    po = torch.empty((B, S, T, Hq, Dv), dtype=torch.float32, device="cuda")
+    pl = torch.empty((B, S, T, Hq), dtype=torch.float32, device="cuda")
+    dcp.dcp_decode_attn_multi_partial(sh, T, q, k, v, inp["block_table"], bounds, po, pl, ws)
+    out = torch.empty((B, T, Hq, Dv), dtype=torch.float32, device="cuda")
+    out_lse = torch.empty((B, T, Hq), dtype=torch.float32, device="cuda")
+    dcp.dcp_decode_attn_multi(sh, T, q, k, v, inp["block_table"], bounds, ws, out, out_lse)
+    torch.cuda.synchronize()
+    assert dcp.dcp_read_device_flags(ws) == 0
+    assert torch.isfinite(out).all() and torch.isfinite(po).all()
+    rng = np.random.default_rng(5)
+    pick = sorted({0, 1, T // 2, T - 2, T - 1} |
+                  set(int(x) for x in rng.choice(T, size=11, replace=False)))
+    _, caches, bt, _ = host_inputs_of(wl, inp)
+    ro, rl = O.partial_attention_multi(wl.kind, wl.dtype, qh, caches, bt,
+                                       np.asarray(bounds_np, np.int64), wl.block_size,
+                                       wl.softmax_scale, Dv, tokens=pick)
+    ro, rl = ro[:, :, pick], rl[:, :, pick]
+    n = len(pick)
+    assert_close(po[:, :, pick].cpu().numpy().reshape(B, S, n * Hq, Dv),
+                 pl[:, :, pick].cpu().numpy().reshape(B, S, n * Hq),
+                 ro.reshape(B, S, n * Hq, Dv), rl.reshape(B, S, n * Hq), wl.dtype,
+                 f"{name} partials")
+    fo, fl = O.merge_lse(ro.reshape(B, S, n * Hq, Dv), rl.reshape(B, S, n * Hq))
+    assert_close(out[:, pick].cpu().numpy().reshape(B, n * Hq, Dv),
+                 out_lse[:, pick].cpu().numpy().reshape(B, n * Hq), fo, fl, wl.dtype,
+                 f"{name} fused")
+
+
 @pytest.mark.parametrize("wl_name,over,lengths", [
     ("mla-64h-b512", dict(batch=3), [1000, 77, 1]),
     ("gqa-g16", dict(batch=3), [2000, 50, 0]),

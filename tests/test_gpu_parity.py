@@ -107,14 +107,18 @@ def test_debug_gather_is_bit_exact(wl_name, over, lengths):
                 assert got.tobytes() == np.ascontiguousarray(want).tobytes(), (b, s, g)
 
 
-def test_device_plan_matches_host_plan():
+def test_device_plan_matches_oracle_plan():
+    """The device plan, bit for bit, against oracle.plan_shards (and the host plan)."""
     say("[gpu] device plan")
     rng = np.random.default_rng(1)
-    for S, bs in ((1, 16), (4, 16), (8, 64), (16, 16), (7, 1)):
+    for S, bs in ((1, 16), (4, 16), (8, 64), (16, 16), (7, 1), (3, 48)):
         lens = rng.integers(0, 1_100_000, size=37).astype(np.int32)
-        lens[:3] = [0, 1, bs]
-        d = dcp.dcp_plan_shards_device(torch.from_numpy(lens).cuda(), S, bs)
-        assert np.array_equal(d.cpu().numpy(), dcp.dcp_plan_shards(lens, S, bs))
+        lens[:5] = [0, 1, bs, bs + 1, S * bs - 1]
+        d = dcp.dcp_plan_shards_device(torch.from_numpy(lens).cuda(), S, bs).cpu().numpy()
+        want = O.plan_shards(lens, S, bs)
+        assert d.dtype == np.int32 and d.shape == want.shape
+        assert np.array_equal(d.astype(np.int64), want), (S, bs)
+        assert np.array_equal(d, dcp.dcp_plan_shards(lens, S, bs))
 
 
 @pytest.mark.parametrize("wl_name,over,lengths", [
