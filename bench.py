@@ -59,6 +59,11 @@ def parse_args():
                    help="query tokens per request (speculative / MTP decode); 1 = plain decode")
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--plant-high-keys", type=float, default=0.0, metavar="FRACTION",
+                   help="MLA only: in this fraction of the requests (seeded), overwrite one "
+                        "latent row in the middle of a random shard with a key that scores "
+                        "90 (natural log units) above the rest for one head, so that the "
+                        "workers meeting it outrun their first tile's maximum")
     p.add_argument("--ceiling-gib", type=float, default=4.0,
                    help="buffer size of the HBM streaming-read ceiling measured in the same run "
                         "(0 skips it)")
@@ -211,6 +216,34 @@ def summarize_mfma(d, workload, family, wl):
         out[key.replace("_per_launch", "") + "_dispatches"] = len(ker)
     out["flops_per_instruction"] = out["mfma_flops_per_launch"] / out["mfma_instructions_per_launch"]
     return out
+
+
+# ------------------------------------------------------------------ planted keys
+
+def plant_high_keys(wl, inp, bounds_np, q_dev, frac, seed=11, score=90.0):
+    """Overwrite one latent row in the middle of a random shard of round(frac * batch)
+    seeded requests with c * q[b, j, h] (bf16), c chosen so that head h of query token j
+    scores `score` above zero on it. Returns the number of requests planted."""
+    import torch
+    rng = np.random.default_rng(seed)
+    n = int(round(frac * wl.batch))
+    bt = inp["block_table_host"]
+    cache = inp["kv_cache"]
+    done = 0
+    for b in rng.choice(wl.batch, size=n, replace=False):
+        b = int(b)
+        s = int(rng.integers(wl.num_shards))
+        lo, hi = (int(x) for x in bounds_np[b, s])
+        if hi - lo < 2:
+            continue
+        t = (lo + hi) // 2
+        h = int(rng.integers(wl.num_q_heads))
+        qh = q_dev[b].reshape(-1, wl.head_dim_qk)[h].float()
+        c = score / (wl.softmax_scale * float(qh @ qh))
+        cache[int(bt[b, t // wl.block_size]), t % wl.block_size] = (c * qh).to(cache.dtype)
+        done += 1
+    torch.cuda.synchronize()
+    return done
 
 
 # ------------------------------------------------------------------ HBM read ceiling
@@ -428,10 +461,21 @@ def main():
         torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
         del a, b
+    planted = None
+    if args.plant_high_keys > 0:
+        if wl.kind != "mla":
+            print("--plant-high-keys applies to MLA workloads", file=sys.stderr)
+            return 2
+        n = plant_high_keys(wl, inp, bounds_np, q_dev, args.plant_high_keys)
+        planted = {"requests": n, "score_nats": 90.0}
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    assert dcp.dcp_read_device_flags(ws) == 0
+    flags = dcp.dcp_read_device_flags(ws)
+    # bits 2 and 3 are informational (a worker recomputed its range, or rescaled in place)
+    assert flags & 3 == 0 and (planted is not None or flags == 0), flags
+    if planted is not None:
+        planted["device_flags"] = flags
     K = args.steps
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
@@ -517,6 +561,7 @@ def main():
         "roofline": roofline,
         "mfma": mfma,
         "hbm_read_ceiling": ceiling,
+        "planted_high_keys": planted,
         "cpu_baseline": cpu,
         "append_kv": append,
     }

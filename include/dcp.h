@@ -247,8 +247,10 @@ dcp_status dcp_decode_attn_multi(const dcp_attn_shape* shape, int32_t q_len, con
  * had end < start. Bit 1: a block id outside [0, num_blocks) was met and its tokens masked.
  * Bit 2 (informational, results unaffected): on the MLA path with 128 query rows per unit, a
  * score exceeded its segment's first-tile maximum by more than 2^64 in weight, and that
- * worker's range was recomputed by the general kernel. Bits are cleared by the next
- * attention call on that workspace.
+ * worker's range was recomputed by the general kernel. Bit 3 (informational, results
+ * unaffected): on the MLA path with 64 query rows per unit, the same happened and that worker
+ * raised the row's reference and rescaled its sum and accumulator in place. Bits are cleared
+ * by the next attention call on that workspace.
  */
 dcp_status dcp_read_device_flags(const void* workspace, int32_t* flags, void* stream);
 

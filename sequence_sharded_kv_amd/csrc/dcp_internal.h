@@ -18,6 +18,7 @@ constexpr int32_t kWsZeroWords = 512;  // 2 KB of zeros
 constexpr int32_t kFlagBoundClamped = 1;
 constexpr int32_t kFlagBadBlock = 2;
 constexpr int32_t kFlagRecomputed = 4;  // a worker's range was recomputed (see mla_pair_kernel)
+constexpr int32_t kFlagRescaled = 8;    // a worker raised a row's reference and rescaled it
 
 // Work is split stream-K style: every (unit, page) pair is one page of work, the pages of
 // all units are concatenated in unit order, and worker w takes the contiguous range

@@ -756,19 +756,14 @@ int32_t mla_mfma_workers(int device, int32_t Ru, int32_t max_workers) {
 
 hipError_t launch_mla_mfma(const AttnArgs& a, hipStream_t stream) {
   const char* zr = a.zero_row;
-  if (a.Ru == 64 || a.Ru == 128) {
+  // 64 rows: the ring kernel, which rescales in place when a reference is raised
+  if (a.Ru == 64) return launch_mla_ring(a, stream);
+  if (a.Ru == 128) {
     // pairs of waves share the value product; workers whose scores outran the fixed
     // reference are recomputed by the 16-rows-per-wave kernel (same worker count)
-    if (a.Ru == 64) {
-      const hipError_t e = launch_mla_ring(a, stream);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((mla_mfma_kernel<4>), dim3(a.P), dim3(256), 0, stream, a, zr,
-                         (const int32_t*)a.redo);
-    } else {
-      hipLaunchKernelGGL((mla_pair_kernel<8>), dim3(a.P), dim3(512), 0, stream, a, zr, a.redo);
-      hipLaunchKernelGGL((mla_mfma_kernel<8>), dim3(a.P), dim3(512), 0, stream, a, zr,
-                         (const int32_t*)a.redo);
-    }
+    hipLaunchKernelGGL((mla_pair_kernel<8>), dim3(a.P), dim3(512), 0, stream, a, zr, a.redo);
+    hipLaunchKernelGGL((mla_mfma_kernel<8>), dim3(a.P), dim3(512), 0, stream, a, zr,
+                       (const int32_t*)a.redo);
     return hipGetLastError();
   }
   const int32_t* none = nullptr;

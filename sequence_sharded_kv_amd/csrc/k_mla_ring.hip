@@ -27,10 +27,13 @@
 // The chunk swizzles, the token permutation and both contractions' LDS addressing are those
 // of mla_pair_kernel.
 //
-// Reference max: the value accumulator is never rescaled. A row's reference m_ref is fixed by
-// the first tile in which it has a valid token (its weights and sum are still zero then). A
-// later score above m_ref + kLazy (exp2 units) marks the worker in `redo`, and
-// mla_mfma_kernel<4> recomputes its whole range afterwards.
+// Reference max: a row's weights are exp2(s - m_ref) with m_ref fixed by the first tile in
+// which the row has a valid token (its weights and sum are still zero then), so the value
+// accumulator is not rescaled tile by tile. Only a later tile whose maximum exceeds
+// m_ref + kLazy (exp2 units; the weights stay below 2^kLazy otherwise) raises the row's
+// reference to that maximum: the score wave scales the row's sum by exp2(m_old - m_new) and
+// posts the factor with the tile's weights, and the value waves scale the row's accumulator
+// by it before they add that tile. Flag bit kFlagRescaled reports that it happened.
 //
 // Waits: a copy wave awaits its copies of a tile with a partial vmcnt (the next tile's copies
 // stay in flight). Tiles that span pages (block sizes below 32, or ranges not aligned to 32
@@ -47,10 +50,14 @@ constexpr int kSlotsB = 3;                        // dims 512..575: 32 rows x 12
 constexpr int kBytesA = 32 * 1024;
 constexpr int kBytesB = 32 * 128;
 constexpr int kOffB = kSlotsA * kBytesA;          // 131072
-constexpr int kXBytes = 4 * 2048;                 // weights of one tile: 4 score waves x 2 KB
+// exchange of one tile: the weights (4 score waves x 2 KB), each row's rescale factor, and one
+// word per score wave telling whether it raised a reference in this tile
+constexpr int kXScale = 4 * 2048;                 // 64 floats
+constexpr int kXFlag = kXScale + 64 * 4;          // 4 words
+constexpr int kXBytes = kXFlag + 64;              // 8512
 constexpr int kOffX = kOffB + kSlotsB * kBytesB;  // 143360
-constexpr int kOffMask = kOffX + 2 * kXBytes;     // 159744: valid-token mask per A slot
-constexpr int kLds = kOffMask + 64;               // 159808 B of the 160 KB
+constexpr int kOffMask = kOffX + 2 * kXBytes;     // 160384: valid-token mask per A slot
+constexpr int kLds = kOffMask + 64;               // 160448 B of the 160 KB
 constexpr int kCopyWave0 = 8;                     // waves 8..11 copy
 constexpr int kWaves = 12;
 constexpr float kLazy = 64.f;
@@ -59,7 +66,7 @@ typedef __attribute__((address_space(4))) const int32_t cint32_t;
 }  // namespace ring
 
 __global__ void __launch_bounds__(64 * ring::kWaves)
-mla_ring_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restrict__ redo) {
+mla_ring_kernel(AttnArgs a, const char* __restrict__ zero_row) {
   using namespace ring;
   __shared__ __attribute__((aligned(1024))) char lds[kLds];
   char* const xch = &lds[kOffX];  // two exchange buffers, tile i in buffer i & 1
@@ -82,7 +89,7 @@ mla_ring_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
   if (g0 >= g1) return;
   int32_t u = find_unit(a.pre, a.U, g0);
   int64_t g = g0;
-  int32_t bad = 0, over = 0;
+  int32_t bad = 0, raised = 0;
   const bool bs_pow2 = (a.bs & (a.bs - 1)) == 0;
   const int bs_shift = __builtin_ctz((unsigned)a.bs);
 
@@ -294,8 +301,16 @@ mla_ring_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
               }
           }
           tmax = quad_max(tmax);
-          if (m_ref == kNegInf) m_ref = tmax;  // first valid tile of the row (O and l are zero)
-          else over |= (tmax > m_ref + kLazy) ? 1 : 0;
+          // first valid tile of the row (O and l are zero): it fixes the reference; a tile
+          // far above it raises the reference, and the row's sum and accumulator are scaled
+          float scale = 1.f;
+          if (m_ref == kNegInf) {
+            m_ref = tmax;
+          } else if (tmax > m_ref + kLazy) {
+            scale = fast_exp2(m_ref - tmax);
+            m_ref = tmax;
+          }
+          const bool raise_any = __ballot(scale != 1.f) != 0;  // wave-uniform
           float pw8[8];
           if (full) {
 #pragma unroll
@@ -320,10 +335,16 @@ mla_ring_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
             hpk[q] = hbits;
             lpk[q] = __builtin_bit_cast(uint32_t, l);
           }
-          l_run += psum;
-          char* xb = xch + (i & 1) * kXBytes + hb * 2048;
+          l_run = l_run * scale + psum;
+          char* xt = xch + (i & 1) * kXBytes;
+          char* xb = xt + hb * 2048;
           *(u32x4*)(xb + lane * 16) = hpk;
           *(u32x4*)(xb + 1024 + lane * 16) = lpk;
+          if (raise_any) {
+            raised = 1;
+            if (gq == 0) ((float*)(xt + kXScale))[16 * hb + n] = scale;
+          }
+          if (lane == 0) ((uint32_t*)(xt + kXFlag))[hb] = raise_any ? 1u : 0u;
         } else {
           // after the last tile: the rows' (l, m) go to the exchange buffer that the last
           // iteration does not read
@@ -360,6 +381,19 @@ mla_ring_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
         const char* xp = xb + 2048 * (2 * rh + (vq & 1)) + 16 * (vn + 32 * (vq >> 1));
         bf16x8 ph = __builtin_bit_cast(bf16x8, *(const u32x4*)xp);
         bf16x8 pl = __builtin_bit_cast(bf16x8, *(const u32x4*)(xp + 1024));
+        // score waves 2 rh and 2 rh + 1 hold this wave's rows: if either raised a reference
+        // at tile i - 1, the rows' accumulators are scaled before that tile is added
+        typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+        const u32x2 rfl = *(const u32x2*)(xb + kXFlag + 8 * rh);
+        if ((rfl[0] | rfl[1]) != 0u) {
+          const int hrow = 32 * rh + (lane & 31);
+          const uint32_t mine = (lane & 31) < 16 ? rfl[0] : rfl[1];
+          const float sc = mine ? ((const float*)(xb + kXScale))[hrow] : 1.f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[k][r] *= sc;
+        }
         auto vread = [&](int step) -> bf16x8 {  // step = 8 s2 + mt
           const int s2 = step >> 3, mt = step & 7;
           const char* v0 = tA + vb + 1024 * s2 + ((32 * (mt ^ s2)) ^ vxq);
@@ -421,15 +455,12 @@ mla_ring_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restri
     g = sg1;
   }
   if (__any(bad) && lane == 0) atomicOr(a.flags, kFlagBadBlock);
-  if (__any(over) && lane == 0) {
-    redo[w] = 1;
-    atomicOr(a.flags, kFlagRecomputed);
-  }
+  if (__any(raised) && lane == 0) atomicOr(a.flags, kFlagRescaled);
 }
 
 hipError_t launch_mla_ring(const AttnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(mla_ring_kernel, dim3(a.P), dim3(64 * ring::kWaves), 0, stream, a,
-                     a.zero_row, a.redo);
+                     a.zero_row);
   return hipGetLastError();
 }
 

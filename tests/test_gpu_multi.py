@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import sequence_sharded_kv_amd as dcp
-from gpu_helpers import assert_close, host_inputs_of, say, shape_of, to_device
+from gpu_helpers import assert_close, host_inputs_of, run_partial, say, shape_of, to_device
 from oracle import oracle as O
 from workloads import make_host_inputs, make_queries, workload
 
@@ -195,12 +195,13 @@ def test_multi_with_one_token_equals_one_token_calls(wl_name, over, lengths):
 
 
 @pytest.mark.parametrize("wl_name", ["mla-128h", "mla-64h-b512"])
-def test_lazy_max_mla_recomputes_workers_whose_scores_outrun_the_first_tile(wl_name):
-    """The wave-pair kernel (8 waves for 128 query rows per unit, 4 for 64) takes weights
-    relative to each segment's first-tile maximum. Two keys planted
-    mid-shard score about 90 (natural log units) above the rest, so those workers are
-    recomputed by the general kernel: the result still matches the oracle and flag bit 2
-    reports the recomputation."""
+def test_lazy_max_mla_handles_scores_that_outrun_the_first_tile(wl_name):
+    """The MLA kernels for 64 and 128 query rows per unit take weights relative to each
+    segment's first-tile maximum. Two keys planted mid-shard score about 90 (natural log
+    units) above the rest. The 128-row kernel's workers that meet them are recomputed by the
+    general kernel (flag bit 2); the 64-row ring kernel raises the rows' reference and rescales
+    their sums and accumulators in place (flag bit 3). Either way the result matches the
+    oracle."""
     from workloads import bf16_bits_from_f32
     say(f"[gpu] lazy-max MLA kernel with planted high-score keys: {wl_name}")
     wl = workload(wl_name).replace(batch=2)
@@ -225,12 +226,60 @@ def test_lazy_max_mla_recomputes_workers_whose_scores_outrun_the_first_tile(wl_n
     dcp.dcp_decode_attn(sh, inp["q"], inp["kv_cache"], None, inp["block_table"], bounds, ws, out,
                         out_lse)
     torch.cuda.synchronize()
-    assert dcp.dcp_read_device_flags(ws) == 4
+    assert dcp.dcp_read_device_flags(ws) == (4 if wl.num_q_heads == 128 else 8)
     hq, caches, bt, lens = host_inputs_of(wl, inp)
     fo, fl = O.full_attention("mla", wl.dtype, hq, caches, bt, lens, bs, wl.softmax_scale,
                               wl.head_dim_v)
     assert float(np.max(fl[0])) > 80.0
     assert_close(out.cpu().numpy(), out_lse.cpu().numpy(), fo, fl, wl.dtype, "planted high score")
+
+
+def test_ring_kernel_raises_the_reference_several_times_in_one_segment():
+    """64 query rows per unit (the ring kernel). In one shard, keys scoring about 90, 180,
+    270 and 360 above the rest for head 0 sit in four consecutive 32-token tiles from the
+    second tile of a page on. A worker covers six or more pages here, so whichever page
+    boundary splits them, one segment meets at least two of them after its first tile and
+    raises that row's reference twice or more. In the other request a high key for head 9
+    raises another row. The rescaled sums and accumulators match the oracle."""
+    from workloads import bf16_bits_from_f32
+    say("[gpu] ring kernel: repeated reference raises in one segment")
+    wl = workload("mla-64h-b512").replace(batch=2)
+    lengths = [60000, 50000]
+    host = make_host_inputs(wl, lengths=lengths)
+    bs = wl.block_size
+
+    def plant(b, t, head, target):
+        qh = (host["q"][b, head].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        c = target / (wl.softmax_scale * float(qh @ qh))
+        host["kv_cache"][host["block_table"][b, t // bs], t % bs] = \
+            bf16_bits_from_f32((c * qh).astype(np.float32))
+
+    bounds_np = dcp.dcp_plan_shards(host["seq_lens"], wl.num_shards, bs)
+    lo, hi = (int(x) for x in bounds_np[0, 1])
+    base = lo + 10 * bs + 32
+    assert base + 128 < hi
+    for k, target in enumerate((90.0, 180.0, 270.0, 360.0)):
+        plant(0, base + 32 * k, 0, target)
+    plant(1, 3500, 9, 90.0)
+    inp = to_device(wl, host)
+    sh = shape_of(wl, inp)
+    bounds = torch.from_numpy(bounds_np).cuda()
+    ws = dcp.alloc_workspace(sh, "cuda")
+    out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim_v), dtype=torch.float32,
+                      device="cuda")
+    out_lse = torch.empty((wl.batch, wl.num_q_heads), dtype=torch.float32, device="cuda")
+    dcp.dcp_decode_attn(sh, inp["q"], inp["kv_cache"], None, inp["block_table"], bounds, ws, out,
+                        out_lse)
+    po, pl, _ = run_partial(wl, inp, bounds, ws=ws)
+    torch.cuda.synchronize()
+    assert dcp.dcp_read_device_flags(ws) == 8
+    hq, caches, bt, lens = host_inputs_of(wl, inp)
+    ro, rl = O.partial_attention("mla", wl.dtype, hq, caches, bt, np.asarray(bounds_np, np.int64),
+                                 bs, wl.softmax_scale, wl.head_dim_v)
+    assert float(rl[0, 1, 0]) > 350.0 and float(rl[1].max()) > 80.0
+    assert_close(po.cpu().numpy(), pl.cpu().numpy(), ro, rl, wl.dtype, "raised, partials")
+    fo, fl = O.merge_lse(ro, rl)
+    assert_close(out.cpu().numpy(), out_lse.cpu().numpy(), fo, fl, wl.dtype, "raised, fused")
 
 
 @pytest.mark.parametrize("wl_name,over,lengths,T", [
