@@ -38,13 +38,13 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "mla": ["k_mla_mfma.hip", "mla_common.h", "device_common.h", "dcp_internal.h"],
     "mla-ring": ["k_mla_ring.hip", "mla_common.h", "device_common.h", "dcp_internal.h"],
-    "mla-pair": ["k_mla_mfma.hip", "mla_common.h", "device_common.h", "dcp_internal.h"],
+    "mla-pair": ["k_mla_pair16.hip", "mla_common.h", "device_common.h", "dcp_internal.h"],
     "gqa-mfma": ["k_gqa_mfma.hip", "device_common.h", "dcp_internal.h"],
     "gqa-chunk": ["k_gqa_chunk.hip", "device_common.h", "dcp_internal.h"],
     "gqa-valu": ["k_gqa_valu.hip", "device_common.h", "dcp_internal.h"],
 }
 KERNEL_NAMES = {"mla": "mla_mfma_kernel", "mla-ring": "mla_ring_kernel",
-                "mla-pair": "mla_pair_kernel",
+                "mla-pair": "mla_pair16_kernel",
                 "gqa-mfma": "gqa_mfma_kernel", "gqa-chunk": "gqa_chunk_kernel",
                 "gqa-valu": "gqa_valu_kernel"}
 
@@ -86,8 +86,8 @@ def parse_args():
 
 def kernel_family(wl, q_len=1):
     if wl.kind == "mla":
-        # units of 64 query rows take the 12-wave ring kernel, of 128 the 8-wave pair kernel,
-        # smaller units the 16-rows-per-wave kernel
+        # units of 64 query rows take the 12-wave ring kernel, of 128 the 8-wave fp16 pair
+        # kernel, smaller units the 16-rows-per-wave kernel
         rows = q_len * wl.num_q_heads
         return "mla-pair" if rows > 64 else "mla-ring" if rows > 32 else "mla"
     g = wl.num_q_heads // wl.num_kv_heads
@@ -203,17 +203,32 @@ def summarize_pmc(fetch_dir, write_dir, workload, family, calib_gib):
 def summarize_mfma(d, workload, family, wl):
     """MFMA counters of the dominant kernel, averaged over its dispatches: MfmaUtil (percent of
     the GPU-active cycles during which the SIMDs' matrix units are busy, summed over SIMDs),
-    MfmaFlopsBF16 (bf16 MFMA operations issued, 512 per MOPS count) and the instruction count.
-    Issued flops include the second value product of the split weights and padding rows."""
+    the matrix operations issued (MfmaFlops over every type, or MfmaFlopsBF16 in older runs;
+    512 per MOPS count) and the bf16 (+ fp16) MFMA instruction count. Issued flops include any
+    second value product of split weights and padding rows."""
     out = {"workload": workload, "kernel": KERNEL_NAMES[family],
            "kernel_sources_sha256": sources_sha(family)}
-    for name, key in (("MfmaUtil", "mfma_busy_pct"), ("MfmaFlopsBF16", "mfma_flops_per_launch"),
-                      ("SQ_INSTS_VALU_MFMA_BF16", "mfma_instructions_per_launch")):
+
+    def mean_of(name, required=True):
         ker = [v for _, k, v in _read_counter_csv(d, name) if KERNEL_NAMES[family] in k]
         if not ker:
-            raise SystemExit(f"{name}: no dispatches of {KERNEL_NAMES[family]} in {d}")
-        out[key] = float(np.mean(ker))
-        out[key.replace("_per_launch", "") + "_dispatches"] = len(ker)
+            if required:
+                raise SystemExit(f"{name}: no dispatches of {KERNEL_NAMES[family]} in {d}")
+            return None, 0
+        return float(np.mean(ker)), len(ker)
+
+    out["mfma_busy_pct"], out["mfma_busy_pct_dispatches"] = mean_of("MfmaUtil")
+    flops, nd = mean_of("MfmaFlops", required=False)
+    if flops is None:
+        flops, nd = mean_of("MfmaFlopsBF16")
+    out["mfma_flops_per_launch"], out["mfma_flops_dispatches"] = flops, nd
+    inst, nd = mean_of("SQ_INSTS_VALU_MFMA_BF16")
+    f16, _ = mean_of("SQ_INSTS_VALU_MFMA_F16", required=False)
+    if f16 is not None:
+        out["mfma_instructions_bf16_per_launch"] = inst
+        out["mfma_instructions_f16_per_launch"] = f16
+        inst += f16
+    out["mfma_instructions_per_launch"], out["mfma_instructions_dispatches"] = inst, nd
     out["flops_per_instruction"] = out["mfma_flops_per_launch"] / out["mfma_instructions_per_launch"]
     return out
 

@@ -30,6 +30,7 @@ SOURCES = [
     ("k_gqa_chunk.hip", "k_gqa_chunk", []),
     ("k_mla_mfma.hip", "k_mla_mfma", []),
     ("k_mla_ring.hip", "k_mla_ring", []),
+    ("k_mla_pair16.hip", "k_mla_pair16", []),
 ]
 
 # -packed-fp32-ops keeps hipcc from emitting packed fp32 VALU ops (v_pk_*_f32).

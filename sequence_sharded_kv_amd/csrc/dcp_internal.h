@@ -17,7 +17,7 @@ constexpr int32_t kWsZeroWords = 512;  // 2 KB of zeros
 // Flag bits in the workspace's sticky device flag word.
 constexpr int32_t kFlagBoundClamped = 1;
 constexpr int32_t kFlagBadBlock = 2;
-constexpr int32_t kFlagRecomputed = 4;  // a worker's range was recomputed (see mla_pair_kernel)
+constexpr int32_t kFlagRecomputed = 4;  // a worker's range was recomputed (see mla_pair16_kernel)
 constexpr int32_t kFlagRescaled = 8;    // a worker raised a row's reference and rescaled it
 
 // Work is split stream-K style: every (unit, page) pair is one page of work, the pages of
@@ -125,6 +125,7 @@ hipError_t launch_gqa_chunk(const AttnArgs& a, hipStream_t stream);
 int32_t mla_mfma_workers(int device, int32_t Ru, int32_t max_workers);
 hipError_t launch_mla_mfma(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_mla_ring(const AttnArgs& a, hipStream_t stream);  // 64 rows per unit
+hipError_t launch_mla_pair16(const AttnArgs& a, hipStream_t stream);  // 128 rows per unit
 hipError_t launch_stream_read(const void* src, size_t bytes, int32_t* sink, int32_t blocks,
                               hipStream_t stream);
 

@@ -303,451 +303,11 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row, const int32_t* __
   if (bad) atomicOr(a.flags, kFlagBadBlock);
 }
 
-// ---------------------------------------------------------------- pairs of waves
-// For 64 query rows per unit (64 heads, the agent-style decode batch) with 4 waves and two
-// workgroups per CU, and for 128 rows (128 heads, or several query tokens of 32 or 64 heads)
-// with 8 waves and one workgroup per CU. The 16x16x32 bf16 MFMA form runs at about half the
-// rate of 32x32x16 here, and the value product (weights split into a bf16 high part and a
-// remainder for accuracy) is two thirds of the matrix work, so this kernel moves the value
-// product onto 32x32x16:
-//   - each wave scores its own 16 rows against the tile exactly as mla_mfma_kernel does
-//     (16x16x32, K from LDS, Q resident);
-//   - waves 2p and 2p + 1 form a pair. Each writes its weights (high part and remainder, 32 B
-//     per lane) to LDS; after a barrier each reads the B operands of two 16-token k steps,
-//     whose columns 0..15 are its own rows and 16..31 its partner's;
-//   - wave 2p + h accumulates O^T for the pair's 32 rows over value dims [256 h, 256 h + 256):
-//     8 accumulator blocks of 32 dims x 32 rows, 32 MFMAs per tile instead of 64.
-// The accumulator (8 blocks of 16 registers) fills the accumulation registers, and scaling
-// it whenever a row's running max moves would cost more than the value product itself. The
-// reference max is therefore fixed by the first tile with a valid token (the accumulator and
-// the sum are still zero then) and weights exp2(x - ref) are taken as they come: they stay
-// finite while x <= ref + kLazy in exp2 units. A score beyond that marks the worker in
-// `redo`, and mla_mfma_kernel<NW> recomputes that worker's whole range afterwards (same
-// units, same pieces). With 4 waves, three of a wave's eight row copies of the next tile and
-// its region-B copy are queued before the scores, the other five after them: a wave stalls
-// while the memory pipeline is full, and an s_memtime breakdown put 26% of a wave-tile in queueing
-// the copies when all nine went first. With 3 first the kernel ran 1-1.5% faster than with 8,
-// 4 or 2; 5 was no faster and 6 slower. With 8 waves a wave copies four rows (two first) and
-// waves 0-3 the region-B blocks; on 128 rows this measured 9-10% faster than a kernel with
-// 32 rows per wave on 32x32x16 for both contractions and a four-tile ring.
-//
-// Tile layout (36 KB, no padding, so that two tiles and the 8 KB weight exchange of each of
-// two 4-wave workgroups fill the 160 KB of LDS): region A = dims 0..511, row r at 1024 r, 16-byte
-// chunk c at position c ^ swz_a(r), swz_a(r) = 2 (r & 15) ^ 32 ((r >> 3) & 1); region B =
-// dims 512..575, row r at 32768 + 128 r, chunk c at c ^ (r & 7). The copies permute the chunks
-// (lane i of a row copy fetches chunk i ^ swz_a(r)). LDS serves 512 bytes per clock here
-// (the bank-conflict counter agrees with that model and not with 256): the score reads of a
-// half-wave (16 rows x 2 chunks) then cover 32 distinct 16-byte bank groups. The rows keep the
-// token permutation pi of mla_mfma_kernel. A value block is dims 16 mt .. + 15 for lane groups
-// 0 and 2 and the same + 128 for groups 1 and 3, which leaves the transposed reads 2-way
-// conflicted in half of the wave (SQ_LDS_BANK_CONFLICT 3.2e8 cycles per launch against 6.4e8
-// for c ^ (r & 15)). A fully conflict-free mapping (32 consecutive dims per block, groups 16
-// dims apart) measured 2.5% slower in the same runs, for reasons the counters do not show.
-namespace pair {
-constexpr int kTile = 32;
-constexpr int kRegionB = 32 * 1024;
-constexpr int kTileBytes = kRegionB + 32 * 128;  // 36864
-template <int NW>  // waves per workgroup (16 rows each)
-struct Cfg {
-  static constexpr int kRows = kTile / NW;      // region-A rows each wave copies per tile
-  static constexpr int kQ0 = NW == 4 ? 3 : 2;   // of them queued before the scores
-  static constexpr int kXBytes = NW * 64 * 32;  // weight exchange: 32 B per lane per wave
-};
-constexpr float kLazy = 64.f;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-// region-A chunk swizzle: bits 1-4 from the row's low four bits, bit 5 from its bit 3
-__device__ __forceinline__ int swz_a(int r) { return mla_swz_a(r); }
-}  // namespace pair
-
-template <int NW>  // 4 waves for 64 rows per unit (two workgroups per CU), 8 for 128 (one)
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
-mla_pair_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __restrict__ redo) {
-  using namespace pair;
-  constexpr int kRows = Cfg<NW>::kRows, kQ0 = Cfg<NW>::kQ0, kXBytes = Cfg<NW>::kXBytes;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * kTileBytes + kXBytes];
-  char* const xch = &lds[2 * kTileBytes];
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
-  const int hw = wv & 1;          // value dims [256 hw, 256 hw + 256)
-  const int pw = wv ^ 1;          // partner wave
-  const int n = lane & 15;        // score layout: head within the wave
-  const int gq = lane >> 4;       // lane quarter
-  const int32_t w = blockIdx.x;
-  if (w >= a.P) return;
-  const uint16_t* __restrict__ Q = (const uint16_t*)a.q;
-  const char* __restrict__ Kc = (const char*)a.k;
-  const int64_t T_pages = a.pre[a.U];
-  const int64_t g0 = worker_begin(T_pages, a.P, w), g1 = worker_begin(T_pages, a.P, w + 1);
-  if (g0 >= g1) return;
-  int32_t u = find_unit(a.pre, a.U, g0);
-  int64_t g = g0;
-  int32_t bad = 0, over = 0;
-  const bool bs_pow2 = (a.bs & (a.bs - 1)) == 0;
-  const int bs_shift = __builtin_ctz((unsigned)a.bs);
-
-  // Per-lane LDS offsets are derived inside the tile loop from an opaque copy of the lane id
-  // (a few VALU operations per tile): held across the loop they would be spilled, and a
-  // reload's wait on the vector memory counter would also wait for the tile copies in flight.
-  // Score reads: lane (n, gq) reads row 16 at + pi(n), chunk 4 j + gq, region A at
-  //   pi(n) 1024 + 16384 at + (64 j ^ 16 (gq ^ swz_a(pi(n)))),
-  // region B (j = 16 + jb) at 32768 + 128 pi(n) + 2048 at + (64 jb ^ 16 (gq ^ (pi(n) & 7))).
-  // Value reads, k step s2: 16-lane group gq, lane 4 i + e reads row pi(4 (s2 + 2 (gq >> 1)) +
-  // i) = 8 (gq >> 1) + 2 i + s2 (+16 for the second half), the 8 bytes of dims 256 hw +
-  // 16 mt + 128 (gq & 1) + 4 e .. + 3, at
-  //   vbase + 1024 s2 + (32 (mt ^ s2) ^ vx).
-  // Weight exchange reads: the B operand of k step s2 holds, in lane rows 0 and 2, this
-  // wave's lanes 32 (gq >> 1) + 16 s2 + n and, in rows 1 and 3, the partner's.
-
-  while (g < g1) {
-    while ((int64_t)a.pre[u + 1] <= g) ++u;
-    const int64_t up0 = a.pre[u], up1 = a.pre[u + 1];
-    const int64_t sg1 = up1 < g1 ? up1 : g1;
-    const int32_t bsi = u / a.NRg, rg = u - bsi * a.NRg;  // (request, shard), row group
-    const int32_t b = bsi / a.S;
-    const int64_t ta = a.ubounds[2 * bsi], te = a.ubounds[2 * bsi + 1];
-    const int64_t pa = ta / a.bs;
-    int64_t t0 = (pa + (g - up0)) * a.bs, t1 = (pa + (sg1 - up0)) * a.bs;
-    if (t0 < ta) t0 = ta;
-    if (t1 > te) t1 = te;
-    const bool whole = (g == up0) && (sg1 == up1);
-    const bool first = (g == g0);
-    const int32_t* brow = a.block_table + (int64_t)b * a.max_blocks;
-
-    // Block id of the page holding token tile + (lane & 31), read one tile ahead of its use.
-    // Token positions fit in 32 bits (max_blocks_per_seq * block_size <= INT32_MAX).
-    const int32_t t0i = (int32_t)t0, t1i = (int32_t)t1;
-    auto page_of = [&](int32_t tile) -> int32_t {
-      int lp = lane;
-      asm volatile("" : "+v"(lp));
-      const int32_t t = tile + (lp & 31);
-      const int32_t tc = t < t1i ? t : t1i - 1;
-      return brow[bs_pow2 ? (tc >> bs_shift) : tc / a.bs];
-    };
-    int32_t blk_next = page_of(t0i);
-
-    // A wave copies region-A rows wv + k NW (k < kRows) and region-B rows 8 wv .. 8 wv + 7 of
-    // each tile.
-    uint64_t row_src[kRows];
-    uint64_t rbase = 0;      // one-page tiles: source of row 0
-    uint32_t rstride = 0;    // one-page tiles: bytes between rows (0 for the zero row)
-    int32_t rlast = 0;       // one-page tiles: last row before t1 (later rows repeat it)
-    int32_t one = 0;         // wave-uniform: the pending tile lies in one page
-    uint32_t base_pend = 0;
-    auto issue_rows = [&](int k0, int k1) {
-      // each row's chunk permutation is formed next to its copy: eight per-lane offsets held
-      // across the tile would be spilled, and a reload's wait would also wait for the copies
-      uint32_t lx16 = 16u * (uint32_t)lane;
-      asm volatile("" : "+v"(lx16));
-      if (one) {
-#pragma unroll
-        for (int k = k0; k < k1; ++k) {
-          const int r = wv + k * NW;
-          const uint32_t rr = (uint32_t)(r < rlast ? r : rlast);
-          dma16s(rbase + (uint64_t)(rr * rstride), lx16 ^ (16u * (uint32_t)swz_a(r)),
-                 base_pend + r * 1024);
-        }
-      } else {
-#pragma unroll
-        for (int k = k0; k < k1; ++k) {
-          const int r = wv + k * NW;
-          dma16s(row_src[k], lx16 ^ (16u * (uint32_t)swz_a(r)), base_pend + r * 1024);
-        }
-      }
-    };
-    auto issue_tile = [&](int32_t tile, int buf, int nrows) -> uint32_t {
-      const int32_t blk = blk_next;
-      if (tile + kTile < t1i) blk_next = page_of(tile + kTile);
-      const uint32_t base = lds_u32(&lds[buf * kTileBytes]);
-      base_pend = base;
-      one = bs_pow2 ? ((tile >> bs_shift) == ((tile + kTile - 1) >> bs_shift))
-                    : (tile / a.bs == (tile + kTile - 1) / a.bs);
-      if (one) {
-        // rows tile .. tile + 31 lie in one page; rows past t1 repeat the last valid row (the
-        // page's later slots may hold anything, and a NaN there would survive its zero weight
-        // in the value product)
-        const int32_t blk1 = __builtin_amdgcn_readfirstlane(blk);
-        const bool page_ok = blk1 >= 0 && blk1 < a.num_blocks;
-        const uint32_t slot0 = bs_pow2 ? (uint32_t)(tile & (a.bs - 1)) : (uint32_t)(tile % a.bs);
-        rbase = page_ok ? (uint64_t)Kc + ((uint64_t)(uint32_t)blk1 * (uint32_t)a.bs + slot0) *
-                                             (kMlaDqk * 2)
-                        : (uint64_t)zero_row;
-        rstride = page_ok ? kMlaDqk * 2 : 0;
-        rlast = t1i - 1 - tile;
-        if (!page_ok) bad = 1;
-        const uint32_t m = (uint32_t)__ballot(page_ok && lane < kTile && tile + lane < t1i);
-        issue_rows(0, nrows);
-        if (NW == 4 || wv < 4) {  // region B: four 1 KB blocks of 8 rows
-          int lb = lane;
-          asm volatile("" : "+v"(lb));
-          const int r = 8 * wv + (lb >> 3);
-          const uint32_t rr = (uint32_t)(r < rlast ? r : rlast);
-          dma16s(rbase, rr * rstride + 1024u + 16u * (uint32_t)((lb & 7) ^ swz_b(r)),
-                 base + kRegionB + wv * 1024);
-        }
-        return m;
-      }
-      uint64_t rowaddr = (uint64_t)zero_row;
-      bool valid = false;
-      if (lane < kTile) {
-        const int32_t t = tile + lane;
-        const int32_t tc = t < t1i ? t : t1i - 1;
-        const bool page_ok = blk >= 0 && blk < a.num_blocks;
-        // row index < num_blocks * block_size rows of 1152 B: below 2^31 for any pool that
-        // fits in device memory
-        const uint32_t slot = bs_pow2 ? (uint32_t)(tc & (a.bs - 1)) : (uint32_t)(tc % a.bs);
-        const uint32_t row = (uint32_t)blk * (uint32_t)a.bs + slot;
-        if (page_ok)
-          rowaddr = (uint64_t)Kc + (uint64_t)row * (kMlaDqk * 2);
-        else
-          bad = 1;
-        valid = page_ok && t < t1i;
-      }
-      const uint32_t mask = (uint32_t)__ballot(valid);
-#pragma unroll
-      for (int k = 0; k < kRows; ++k) row_src[k] = readlane_u64(rowaddr, wv + k * NW);
-      issue_rows(0, kRows);
-      if (NW == 4 || wv < 4) {
-        // lane covers row 8 wv + lane / 8: pick its address among the eight rows' addresses
-        uint64_t ra = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint64_t aj = readlane_u64(rowaddr, 8 * wv + j);
-          ra = ((lane >> 3) == j) ? aj : ra;
-        }
-        int lb = lane;
-        asm volatile("" : "+v"(lb));
-        const int r = 8 * wv + (lb >> 3);
-        dma16((const char*)ra + 1024 + 16 * ((lb & 7) ^ swz_b(r)),
-              base + kRegionB + wv * 1024);
-      }
-      return mask;
-    };
-
-    // This wave's 16 query rows and the last context position they may see.
-    int32_t jq = 0;
-    const int32_t rho_s = unit_row(a, 0, rg, 16 * wv + n, &jq);
-    const int32_t lim = a.Tq == 1 ? INT32_MAX
-                                  : __builtin_amdgcn_readfirstlane(a.qend[b] + jq);
-    bf16x8 qop[kMlaDqk / 32];
-    {
-      const uint16_t* qrow =
-          Q + ((int64_t)b * a.R + (rho_s >= 0 ? rho_s : 0)) * kMlaDqk + 8 * gq;
-#pragma unroll
-      for (int j = 0; j < kMlaDqk / 32; ++j)
-        qop[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 32 * j));
-    }
-
-    f32x16 acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-    float m_ref = kNegInf, l_run = 0.f;
-
-    uint32_t mask_next = issue_tile(t0i, 0, kRows);
-    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) lgkmcnt(0): the copies of the first tile
-    __syncthreads();
-    int cur = 0;
-    for (int32_t tile = t0i; tile < t1i; tile += kTile) {
-      const int32_t dl = lim - tile;
-      const uint32_t mask =
-          mask_next & (dl < 0 ? 0u : dl >= kTile - 1 ? 0xFFFFFFFFu : (2u << dl) - 1u);
-      const bool more = tile + kTile < t1i;
-      // copies are queued at raised wave priority too (see the value loop)
-      __builtin_amdgcn_s_setprio(1);
-      if (more) mask_next = issue_tile(tile + kTile, cur ^ 1, kQ0);
-      __builtin_amdgcn_s_setprio(0);
-      const char* tb = &lds[cur * kTileBytes];
-
-      // S^T = K . Q^T for the two 16-row subtiles
-      int lk = lane;
-      asm volatile("" : "+v"(lk));
-      const int kr0 = tok_of_row(lk & 15), kq = lk >> 4;
-      const int kb = kr0 * 1024, kxq = 16 * (kq ^ swz_a(kr0));
-      const int kbB = kRegionB + kr0 * 128, kxBq = 16 * (kq ^ (kr0 & 7));
-      // The two subtiles' chains alternate and the K reads run kPre ahead: left to the
-      // compiler, one chain ran after the other with one read in flight, each MFMA waiting on
-      // its read and on the previous MFMA.
-      auto kread = [&](int idx) -> bf16x8 {  // idx = 2 j + at
-        const int at = idx & 1, j = idx >> 1;
-        const char* p = (j < 16) ? tb + kb + 16384 * at + ((64 * j) ^ kxq)
-                                 : tb + kbB + 2048 * at + ((64 * (j - 16)) ^ kxBq);
-        return __builtin_bit_cast(bf16x8, *(const u32x4*)p);
-      };
-      constexpr int kPre = 4;
-      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      bf16x8 kbuf[kPre];
-#pragma unroll
-      for (int q = 0; q < kPre; ++q) kbuf[q] = kread(q);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int idx = 0; idx < 2 * (kMlaDqk / 32); ++idx) {
-        const bf16x8 kop = kbuf[idx % kPre];
-        if (idx + kPre < 2 * (kMlaDqk / 32)) kbuf[idx % kPre] = kread(idx + kPre);
-        s[idx & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[idx >> 1], s[idx & 1], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-
-      __builtin_amdgcn_s_setprio(1);
-      if (more && one) issue_rows(kQ0, kRows);  // the rest of a one-page tile's row copies
-      __builtin_amdgcn_s_setprio(0);
-      // weights against the fixed reference; s[at][i] is MFMA row 4gq + i of subtile at. The
-      // mask is wave-uniform; a tile with every token visible (all but a segment's edges)
-      // skips the per-score masking and the -inf guards.
-      float x[8];
-      float tmax = kNegInf;
-      const bool full = mask == 0xFFFFFFFFu;
-      if (full) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          x[k] = s[k >> 2][k & 3] * a.scale_log2;
-          tmax = fmaxf(tmax, x[k]);
-        }
-      } else {
-        // per-lane token positions formed here (held across the loop they would be spilled)
-        int lm = lane;
-        asm volatile("" : "+v"(lm));
-        const int gqm = lm >> 4;
-#pragma unroll
-        for (int at = 0; at < 2; ++at)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tok = 16 * at + tok_of_row(4 * gqm + i);
-            const float v = ((mask >> tok) & 1u) ? s[at][i] * a.scale_log2 : kNegInf;
-            x[4 * at + i] = v;
-            tmax = fmaxf(tmax, v);
-          }
-      }
-      tmax = quad_max(tmax);
-      if (m_ref == kNegInf) m_ref = tmax;  // first valid tile of the row (O and l are zero)
-      else over |= (tmax > m_ref + kLazy) ? 1 : 0;
-      float pw8[8];
-      if (full) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) pw8[k] = fast_exp2(x[k] - m_ref);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) pw8[k] = (x[k] == kNegInf) ? 0.f : fast_exp2(x[k] - m_ref);
-      }
-      // bf16 high parts packed in pairs, the remainders from the unpacked highs
-      float psum = 0.f;
-      u32x4 hpk, lpk;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float p0 = pw8[2 * q], p1 = pw8[2 * q + 1];
-        psum += p0 + p1;
-        typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-        const bf16x2 h = {(__bf16)p0, (__bf16)p1};
-        const uint32_t hb = __builtin_bit_cast(uint32_t, h);
-        const float r0 = p0 - __uint_as_float(hb << 16);
-        const float r1 = p1 - __uint_as_float(hb & 0xFFFF0000u);
-        const bf16x2 l = {(__bf16)r0, (__bf16)r1};
-        hpk[q] = hb;
-        lpk[q] = __builtin_bit_cast(uint32_t, l);
-      }
-      const bf16x8 phi = __builtin_bit_cast(bf16x8, hpk), plo = __builtin_bit_cast(bf16x8, lpk);
-      l_run += psum;
-
-      // hand the weights to the partner wave
-      *(u32x4*)(xch + wv * 2048 + lane * 16) = __builtin_bit_cast(u32x4, phi);
-      *(u32x4*)(xch + wv * 2048 + 1024 + lane * 16) = __builtin_bit_cast(u32x4, plo);
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      // O^T[256 dims x 32 rows] += V^T . P over two 16-token k steps; B operand columns
-      // 0..15 = own rows, 16..31 = partner rows; k step 0 holds the tokens of lane quarters 0
-      // and 2 of the score layout, k step 1 those of quarters 1 and 3
-      int lv = lane;
-      asm volatile("" : "+v"(lv));
-      const int vn = lv & 15, vq = lv >> 4;
-      const int vrow0 = 8 * (vq >> 1) + 2 * (vn >> 2);
-      const int vb = vrow0 * 1024 + 512 * (hw ^ (vq >> 1)) + 8 * (vn & 1);
-      const int vxq = 16 * (((16 * (vq & 1)) | ((vn & 3) >> 1)) ^ (2 * vrow0));
-      const int xo = 2048 * ((vq & 1) ? pw : wv) + 16 * (vn + 32 * (vq >> 1));
-      // the weights of both k steps first, then the V operands kVPre ahead of their MFMAs
-      const bf16x8 ph[2] = {__builtin_bit_cast(bf16x8, *(const u32x4*)(xch + xo)),
-                            __builtin_bit_cast(bf16x8, *(const u32x4*)(xch + xo + 256))};
-      const bf16x8 pl[2] = {__builtin_bit_cast(bf16x8, *(const u32x4*)(xch + xo + 1024)),
-                            __builtin_bit_cast(bf16x8, *(const u32x4*)(xch + xo + 1280))};
-      auto vread = [&](int step) -> bf16x8 {  // step = 8 s2 + mt
-        const int s2 = step >> 3, mt = step & 7;
-        const char* v0 = tb + vb + 1024 * s2 + ((32 * (mt ^ s2)) ^ vxq);
-        return mla_tr_pair(v0, v0 + 16 * 1024);
-      };
-      // the value MFMAs and the copy issue run at raised wave priority, the scores and the
-      // softmax at the base level: a wave that multiplies or queues copies goes first (about
-      // 1% faster per launch for each of the two)
-      __builtin_amdgcn_s_setprio(1);
-      constexpr int kVPre = 2;
-      bf16x8 vbuf[kVPre];
-#pragma unroll
-      for (int q = 0; q < kVPre; ++q) vbuf[q] = vread(q);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int step = 0; step < 16; ++step) {
-        const int s2 = step >> 3, mt = step & 7;
-        const bf16x8 vop = vbuf[step % kVPre];
-        if (step + kVPre < 16) vbuf[step % kVPre] = vread(step + kVPre);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, ph[s2], acc[mt], 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pl[s2], acc[mt], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) lgkmcnt(0): the next tile's copies landed
-      __syncthreads();
-      cur ^= 1;
-    }
-
-    // finalise: every wave is past the last tile's barrier, so the exchange area is free
-    {
-      const float l_own = quad_sum(l_run);
-      float* xf = (float*)xch;
-      if (gq == 0) {
-        xf[2 * (16 * wv + n)] = l_own;
-        xf[2 * (16 * wv + n) + 1] = m_ref;
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const int c32 = lane & 31;
-    const int hrow = c32 < 16 ? 16 * wv + c32 : 16 * pw + (c32 - 16);  // row within the unit
-    const float lc = ((const float*)xch)[2 * hrow];
-    const float mc = ((const float*)xch)[2 * hrow + 1];
-    int32_t jr = 0;
-    const int32_t rho = unit_row(a, 0, rg, hrow, &jr);
-    const float inv = lc > 0.f ? 1.f / lc : 0.f;
-    float* dst_o;
-    float* dst_l;
-    if (whole) {
-      dst_o = a.part_o + ((int64_t)bsi * a.R + (rho >= 0 ? rho : 0)) * kMlaDv;
-      dst_l = a.part_lse + (int64_t)bsi * a.R + (rho >= 0 ? rho : 0);
-    } else {
-      const int32_t slot = piece_slot(w, first);
-      dst_o = a.piece_o + ((int64_t)slot * a.Ru + hrow) * kMlaDv;
-      dst_l = a.piece_lse + (int64_t)slot * a.Ru + hrow;
-    }
-    if (rho >= 0) {
-      // acc[mt][4 qd + i] is dim 256 hw + 16 mt + 128 (qd >> 1) + 8 (qd & 1) + 4 (lane >> 5) + i
-      const int dbase = 256 * hw + 4 * (lane >> 5);
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          *(f32x4*)(dst_o + dbase + 16 * mt + 128 * (qd >> 1) + 8 * (qd & 1)) =
-              f32x4{acc[mt][4 * qd], acc[mt][4 * qd + 1], acc[mt][4 * qd + 2],
-                    acc[mt][4 * qd + 3]} * inv;
-      if (lane < 16) *dst_l = lc > 0.f ? (mc + fast_log2(lc)) * kLn2 : kNegInf;
-    }
-    g = sg1;
-  }
-  if (__any(bad) && lane == 0) atomicOr(a.flags, kFlagBadBlock);
-  if (__any(over) && lane == 0) {
-    redo[w] = 1;
-    atomicOr(a.flags, kFlagRecomputed);
-  }
-}
-
 int32_t mla_mfma_workers(int device, int32_t Ru, int32_t max_workers) {
-  // 64 rows: one 12-wave ring workgroup per CU (156 KB of LDS). Otherwise LDS (2 x 36.5 KB per
-  // workgroup) allows two resident workgroups per CU and registers two waves per SIMD, so two
-  // workgroups fit while a workgroup has at most four waves.
+  // 64 rows: one 12-wave ring workgroup per CU (157 KB of LDS); 128 rows: one 8-wave fp16
+  // workgroup per CU. Otherwise LDS (2 x 36.5 KB per workgroup) allows two resident
+  // workgroups per CU and registers two waves per SIMD, so two workgroups fit while a
+  // workgroup has at most four waves.
   const int nw = Ru / 16;
   const int per_cu = (Ru == 64 || nw > 4) ? 1 : 2;
   int32_t p = mla_cus(device) * per_cu;
@@ -759,9 +319,10 @@ hipError_t launch_mla_mfma(const AttnArgs& a, hipStream_t stream) {
   // 64 rows: the ring kernel, which rescales in place when a reference is raised
   if (a.Ru == 64) return launch_mla_ring(a, stream);
   if (a.Ru == 128) {
-    // pairs of waves share the value product; workers whose scores outran the fixed
-    // reference are recomputed by the 16-rows-per-wave kernel (same worker count)
-    hipLaunchKernelGGL((mla_pair_kernel<8>), dim3(a.P), dim3(512), 0, stream, a, zr, a.redo);
+    // pairs of waves share an fp16 value product; workers whose values fp16 cannot hold are
+    // recomputed in bf16 by the 16-rows-per-wave kernel (same worker count)
+    const hipError_t e = launch_mla_pair16(a, stream);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((mla_mfma_kernel<8>), dim3(a.P), dim3(512), 0, stream, a, zr,
                        (const int32_t*)a.redo);
     return hipGetLastError();

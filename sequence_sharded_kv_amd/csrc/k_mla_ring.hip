@@ -24,8 +24,7 @@
 // and the softmax) beside one value wave (32 MFMAs). The latent dims 0..511 of a tile (32 KB)
 // live in a four-slot ring, since the value product reads them one iteration after the scores;
 // the rope dims 512..575 (4 KB) in a three-slot ring; the exchange is double-buffered.
-// The chunk swizzles, the token permutation and both contractions' LDS addressing are those
-// of mla_pair_kernel.
+// The tile layout (chunk swizzles, token permutation) is the one in mla_common.h.
 //
 // Reference max: a row's weights are exp2(s - m_ref) with m_ref fixed by the first tile in
 // which the row has a valid token (its weights and sum are still zero then), so the value

@@ -198,10 +198,8 @@ def test_multi_with_one_token_equals_one_token_calls(wl_name, over, lengths):
 def test_lazy_max_mla_handles_scores_that_outrun_the_first_tile(wl_name):
     """The MLA kernels for 64 and 128 query rows per unit take weights relative to each
     segment's first-tile maximum. Two keys planted mid-shard score about 90 (natural log
-    units) above the rest. The 128-row kernel's workers that meet them are recomputed by the
-    general kernel (flag bit 2); the 64-row ring kernel raises the rows' reference and rescales
-    their sums and accumulators in place (flag bit 3). Either way the result matches the
-    oracle."""
+    units) above the rest: the workers that meet them raise the rows' reference and rescale
+    their sums and accumulators in place (flag bit 3), and the result matches the oracle."""
     from workloads import bf16_bits_from_f32
     say(f"[gpu] lazy-max MLA kernel with planted high-score keys: {wl_name}")
     wl = workload(wl_name).replace(batch=2)
@@ -226,12 +224,62 @@ def test_lazy_max_mla_handles_scores_that_outrun_the_first_tile(wl_name):
     dcp.dcp_decode_attn(sh, inp["q"], inp["kv_cache"], None, inp["block_table"], bounds, ws, out,
                         out_lse)
     torch.cuda.synchronize()
-    assert dcp.dcp_read_device_flags(ws) == (4 if wl.num_q_heads == 128 else 8)
+    assert dcp.dcp_read_device_flags(ws) == 8
     hq, caches, bt, lens = host_inputs_of(wl, inp)
     fo, fl = O.full_attention("mla", wl.dtype, hq, caches, bt, lens, bs, wl.softmax_scale,
                               wl.head_dim_v)
     assert float(np.max(fl[0])) > 80.0
     assert_close(out.cpu().numpy(), out_lse.cpu().numpy(), fo, fl, wl.dtype, "planted high score")
+
+
+@pytest.mark.parametrize("case", ["huge-value", "tiny-values"])
+def test_fp16_value_kernel_recomputes_what_fp16_cannot_hold(case):
+    """128 query rows per unit take the value product in fp16. A latent value of 70000
+    (beyond fp16's 65504) in one request, or a request whose latent rows are all scaled
+    below 2^-10, sends the workers that meet them to the bf16 kernel (flag bit 2); the
+    result matches the oracle."""
+    from workloads import bf16_bits_from_f32
+    say(f"[gpu] fp16 value range: {case}")
+    wl = workload("mla-128h").replace(batch=2)
+    lengths = [1500, 700]
+    host = make_host_inputs(wl, lengths=lengths)
+    bs = wl.block_size
+    cache = host["kv_cache"]
+    if case == "huge-value":
+        t = 900
+        row = (cache[host["block_table"][0, t // bs], t % bs].astype(np.uint32) << 16) \
+            .view(np.float32).copy()
+        row[5] = 70000.0
+        cache[host["block_table"][0, t // bs], t % bs] = bf16_bits_from_f32(row)
+    else:
+        pages = host["block_table"][1, : -(-lengths[1] // bs)]
+        vals = (cache[pages].astype(np.uint32) << 16).view(np.float32)
+        cache[pages] = bf16_bits_from_f32((vals * 2.0 ** -12).astype(np.float32))
+    inp = to_device(wl, host)
+    sh = shape_of(wl, inp)
+    bounds_np = dcp.dcp_plan_shards(host["seq_lens"], wl.num_shards, bs)
+    bounds = torch.from_numpy(bounds_np).cuda()
+    ws = dcp.alloc_workspace(sh, "cuda")
+    out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim_v), dtype=torch.float32,
+                      device="cuda")
+    out_lse = torch.empty((wl.batch, wl.num_q_heads), dtype=torch.float32, device="cuda")
+    dcp.dcp_decode_attn(sh, inp["q"], inp["kv_cache"], None, inp["block_table"], bounds, ws, out,
+                        out_lse)
+    torch.cuda.synchronize()
+    assert dcp.dcp_read_device_flags(ws) & 4
+    hq, caches, bt, lens = host_inputs_of(wl, inp)
+    fo, fl = O.full_attention("mla", wl.dtype, hq, caches, bt, lens, bs, wl.softmax_scale,
+                              wl.head_dim_v)
+    if case == "tiny-values":
+        assert_close(out.cpu().numpy(), out_lse.cpu().numpy(), fo, fl, wl.dtype, case)
+    else:
+        # outputs and LSEs reach about 7e4 and 5e3 here: the bounds are relative to them
+        got, lse = out.cpu().numpy().astype(np.float64), out_lse.cpu().numpy().astype(np.float64)
+        scale = max(1.0, float(np.abs(fo).max()))
+        assert np.all(np.isfinite(got))
+        assert float(np.abs(got - fo).max()) <= 2e-3 * scale
+        assert float(np.linalg.norm(got - fo) / np.linalg.norm(fo)) <= 1e-3
+        assert float(np.abs(lse - fl).max()) <= 1e-3 * max(1.0, float(np.abs(fl).max()))
 
 
 def test_ring_kernel_raises_the_reference_several_times_in_one_segment():
@@ -285,8 +333,8 @@ def test_ring_kernel_raises_the_reference_several_times_in_one_segment():
 @pytest.mark.parametrize("wl_name,over,lengths,T", [
     ("gqa-g16", dict(batch=2), [300, 200], 4),       # 64 rows per KV head: gqa_chunk_kernel
     ("mla-64h-b512", dict(batch=2), [300, 200], 1),  # 64 rows: mla_ring_kernel
-    ("mla-64h-b512", dict(batch=2), [300, 200], 2),  # 128 rows: mla_pair_kernel<8>
-    ("mla-128h", dict(batch=2), [300, 200], 1),      # 128 heads: mla_pair_kernel<8>
+    ("mla-64h-b512", dict(batch=2), [300, 200], 2),  # 128 rows: mla_pair16_kernel
+    ("mla-128h", dict(batch=2), [300, 200], 1),      # 128 heads: mla_pair16_kernel
 ])
 def test_multi_row_kernels_flag_invalid_device_values(wl_name, over, lengths, T):
     """The kernels for many rows per KV tile mask a block id outside the pool and clamp a
