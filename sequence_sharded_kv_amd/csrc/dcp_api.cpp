@@ -172,6 +172,8 @@ dcp_status make_plan(const dcp_attn_shape* sh, int32_t Tq, dcp::Plan* plan) {
   w.ubounds = off;     off = align_up(off + sizeof(int32_t) * B * S * 2);
   w.qend = off;        off = align_up(off + sizeof(int32_t) * B);
   w.redo = off;        off = align_up(off + sizeof(int32_t) * (size_t)pmax);
+  w.usrc = off;        off = align_up(off + sizeof(int32_t) * 4 * (size_t)units);
+  w.wbeg = off;        off = align_up(off + sizeof(int32_t) * ((size_t)pmax + 1));
   w.piece_o = off;     off = align_up(off + sizeof(float) * 2 * (size_t)pmax * ru * Dv);
   w.piece_lse = off;   off = align_up(off + sizeof(float) * 2 * (size_t)pmax * ru);
   w.part_o = off;      off = align_up(off + sizeof(float) * B * S * R * Dv);
@@ -219,6 +221,8 @@ dcp_status run_partials(const dcp_attn_shape* sh, int32_t Tq, const void* q, con
   a.ubounds = reinterpret_cast<int32_t*>(ws + plan.ws.ubounds);
   a.pre = reinterpret_cast<int32_t*>(ws + plan.ws.pre);
   a.fin = reinterpret_cast<int32_t*>(ws + plan.ws.fin);
+  a.usrc = reinterpret_cast<int32_t*>(ws + plan.ws.usrc);
+  a.wbeg = reinterpret_cast<int32_t*>(ws + plan.ws.wbeg);
   a.qend = reinterpret_cast<int32_t*>(ws + plan.ws.qend);
   a.redo = reinterpret_cast<int32_t*>(ws + plan.ws.redo);
   a.part_o = fused ? reinterpret_cast<float*>(ws + plan.ws.part_o) : part_o;
@@ -255,7 +259,8 @@ dcp_status run_partials(const dcp_attn_shape* sh, int32_t Tq, const void* q, con
   e = dcp::launch_schedule(bounds, a.B, a.S, units_per_bs, a.P,
                            reinterpret_cast<int32_t*>(ws + plan.ws.fin), a.bs, a.max_blocks,
                            const_cast<int32_t*>(a.ubounds), const_cast<int32_t*>(a.pre), a.flags,
-                           Tq, const_cast<int32_t*>(a.qend), a.redo, s);
+                           Tq, const_cast<int32_t*>(a.qend), a.redo,
+                           const_cast<int32_t*>(a.usrc), const_cast<int32_t*>(a.wbeg), s);
   if (e != hipSuccess) return device_fail(e, "schedule launch");
   const bool timed = g_timing.on && g_timing.used < g_timing.start.size();
   if (timed) {
@@ -274,8 +279,10 @@ dcp_status run_partials(const dcp_attn_shape* sh, int32_t Tq, const void* q, con
     e = hipEventRecord(g_timing.stop[g_timing.used++], s);
     if (e != hipSuccess) return device_fail(e, "timing event");
   }
-  e = dcp::launch_finish_units(a, s);
-  if (e != hipSuccess) return device_fail(e, "finish launch");
+  if (!fused) {  // the fused calls combine pieces and partials in one pass instead
+    e = dcp::launch_finish_units(a, s);
+    if (e != hipSuccess) return device_fail(e, "finish launch");
+  }
   *plan_out = plan;
   *args_out = a;
   return DCP_OK;
@@ -398,9 +405,8 @@ dcp_status dcp_decode_attn_multi(const dcp_attn_shape* shape, int32_t q_len, con
   dcp_status st = run_partials(shape, q_len, q, k_cache, v_cache, block_table, bounds, nullptr,
                                nullptr, workspace, workspace_bytes, stream, &plan, &a, true);
   if (st != DCP_OK) return st;
-  hipError_t e = dcp::launch_merge(a.B, a.S, a.R, a.Dv, a.part_o, a.part_lse, out, out_lse,
-                                   as_stream(stream));
-  if (e != hipSuccess) return device_fail(e, "merge launch");
+  hipError_t e = dcp::launch_combine(a, out, out_lse, as_stream(stream));
+  if (e != hipSuccess) return device_fail(e, "combine launch");
   return ok();
 }
 

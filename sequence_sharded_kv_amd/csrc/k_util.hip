@@ -37,21 +37,25 @@ hipError_t launch_plan_device(const int32_t* seq_lens, int32_t B, int32_t S, int
 // One workgroup: sanitise the bounds of every (request, shard), count each unit's pages and
 // write the exclusive prefix sum pre[0..U] (units ordered (b, s, h) with h < units_per_bs).
 // A second pass lists the units the finishing pass must write (cut by a worker boundary, or
-// without pages) in `fin`, with their count in flags[1]. Also clears the flag word (the
-// first call of a step owns it) and the P recomputation marks.
+// without pages) in `fin`, with their count in flags[1], records who wrote each unit in
+// `usrc` and each worker's first page in `wbeg` (for the combining pass). Also clears the
+// flag word (the first call of a step owns it) and the P recomputation marks.
 constexpr int kSchedThreads = 1024;
+constexpr int kSchedPer = 4;  // consecutive units per thread in one pass of the scan
 
 __global__ void __launch_bounds__(kSchedThreads)
 schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_t units_per_bs,
                 int32_t P, int32_t* __restrict__ fin, int32_t bs, int32_t max_blocks,
                 int32_t* __restrict__ ubounds, int32_t* __restrict__ pre,
                 int32_t* __restrict__ flags, int32_t Tq, int32_t* __restrict__ qend,
-                int32_t* __restrict__ redo) {
+                int32_t* __restrict__ redo, int32_t* __restrict__ usrc,
+                int32_t* __restrict__ wbeg) {
   __shared__ int32_t warp_sums[kSchedThreads / 64];
   __shared__ int32_t carry;
   __shared__ int32_t flag_acc;
   __shared__ int32_t fin_count;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   if (tid == 0) { carry = 0; flag_acc = 0; fin_count = 0; }
   for (int i = tid; i < kWsZeroWords; i += kSchedThreads) flags[kWsZeroOffset / 4 + i] = 0;
   for (int i = tid; i < P; i += kSchedThreads) redo[i] = 0;
@@ -59,35 +63,46 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
   const int64_t cap = (int64_t)max_blocks * bs;
   const int64_t nbs = (int64_t)B * S;
   const int64_t U = nbs * units_per_bs;
+  // consecutive units per thread: as few as cover the units in one pass (up to kSchedPer)
+  const int32_t per = U <= kSchedThreads ? 1 : U <= 2 * kSchedThreads ? 2 : kSchedPer;
+  const int64_t pass = (int64_t)kSchedThreads * per;
   int32_t my_flag = 0;
-  for (int64_t base = 0; base < U; base += kSchedThreads) {
-    int64_t u = base + tid;
-    int32_t cnt = 0;
-    if (u < U) {
-      // U * max_blocks fits in 32 bits (checked by the host plan), so unit indices do too
-      const int64_t bsi = (int64_t)((uint32_t)u / (uint32_t)units_per_bs);
-      int64_t a = bounds[2 * bsi], e = bounds[2 * bsi + 1];
-      int64_t a0 = a, e0 = e;
-      if (a < 0) a = 0;
-      if (e > cap) e = cap;
-      if (a > cap) a = cap;
-      if (e < a) e = a;
-      if (a != a0 || e != e0) my_flag |= kFlagBoundClamped;
-      if ((uint32_t)u - (uint32_t)bsi * (uint32_t)units_per_bs == 0) {
-        ubounds[2 * bsi] = (int32_t)a;
-        ubounds[2 * bsi + 1] = (int32_t)e;
+  // page offsets and counts of this thread's units in the last pass (all of them when one
+  // pass covers every unit)
+  int32_t p0s[kSchedPer], cnts[kSchedPer];
+  for (int64_t base = 0; base < U; base += pass) {
+    // U * max_blocks fits in 32 bits (checked by the host plan), so unit indices do too
+    const int64_t u0 = base + (int64_t)tid * per;
+    int32_t tot = 0;
+#pragma unroll
+    for (int k = 0; k < kSchedPer; ++k) {
+      const int64_t u = u0 + k;
+      cnts[k] = 0;
+      if (k < per && u < U) {
+        const int64_t bsi = (int64_t)((uint32_t)u / (uint32_t)units_per_bs);
+        int64_t a = bounds[2 * bsi], e = bounds[2 * bsi + 1];
+        const int64_t a0 = a, e0 = e;
+        if (a < 0) a = 0;
+        if (e > cap) e = cap;
+        if (a > cap) a = cap;
+        if (e < a) e = a;
+        if (a != a0 || e != e0) my_flag |= kFlagBoundClamped;
+        if ((uint32_t)u - (uint32_t)bsi * (uint32_t)units_per_bs == 0) {
+          ubounds[2 * bsi] = (int32_t)a;
+          ubounds[2 * bsi + 1] = (int32_t)e;
+        }
+        // 0 <= a <= e <= cap <= INT32_MAX: 32-bit page arithmetic
+        cnts[k] = (e > a) ? (int32_t)(((uint32_t)e + (uint32_t)bs - 1u) / (uint32_t)bs -
+                                      (uint32_t)a / (uint32_t)bs)
+                          : 0;
       }
-      // 0 <= a <= e <= cap <= INT32_MAX: 32-bit page arithmetic
-      cnt = (e > a) ? (int32_t)(((uint32_t)e + (uint32_t)bs - 1u) / (uint32_t)bs -
-                                (uint32_t)a / (uint32_t)bs)
-                    : 0;
+      tot += cnts[k];
     }
-    // inclusive scan within the wave
-    int lane = tid & 63, wv = tid >> 6;
-    int32_t x = cnt;
+    // exclusive scan of the threads' totals: within the wave, then over the waves
+    int32_t x = tot;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      int32_t y = __shfl_up(x, off, 64);
+      const int32_t y = __shfl_up(x, off, 64);
       if (lane >= off) x += y;
     }
     if (lane == 63) warp_sums[wv] = x;
@@ -96,28 +111,33 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
       int32_t ws = (lane < kSchedThreads / 64) ? warp_sums[lane] : 0;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        int32_t y = __shfl_up(ws, off, 64);
+        const int32_t y = __shfl_up(ws, off, 64);
         if (lane >= off) ws += y;
       }
       if (lane < kSchedThreads / 64) warp_sums[lane] = ws;  // inclusive over waves
     }
     __syncthreads();
-    int32_t excl = carry + (wv > 0 ? warp_sums[wv - 1] : 0) + x - cnt;
-    if (u < U) pre[u] = excl;
-    __syncthreads();
-    if (tid == kSchedThreads - 1) carry = excl + cnt;
+    int32_t run = carry + (wv > 0 ? warp_sums[wv - 1] : 0) + x - tot;
+#pragma unroll
+    for (int k = 0; k < kSchedPer; ++k) {
+      p0s[k] = run;
+      if (k < per && u0 + k < U) pre[u0 + k] = run;
+      run += cnts[k];
+    }
+    __syncthreads();  // every thread has read carry
+    if (tid == kSchedThreads - 1) carry = run;
     __syncthreads();
   }
   if (my_flag) atomicOr(&flag_acc, my_flag);
-  if (tid == 0) pre[U] = carry;
-  __syncthreads();  // pre[] and ubounds[] are complete and visible to the workgroup
+  const int64_t T = carry;
+  if (tid == 0) pre[U] = (int32_t)T;
+  __syncthreads();  // ubounds[] is complete and visible to the workgroup
   // position of each request's first query token: the end of its ranges minus Tq
   for (int64_t b = tid; b < B; b += kSchedThreads) {
     int32_t end = 0;
     for (int32_t sh = 0; sh < S; ++sh) end = max(end, ubounds[2 * (b * S + sh) + 1]);
     qend[b] = end - Tq;
   }
-  const int64_t T = carry;
   // worker_of in 32-bit unsigned arithmetic when (T + 1) * P fits (the same quotients; the
   // 64-bit divisions cost more than the rest of this pass)
   const bool narrow = (T + 1) * (int64_t)P < ((int64_t)1 << 32);
@@ -128,16 +148,35 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
     }
     return worker_of(T, P, g);
   };
-  for (int64_t u = tid; u < U; u += kSchedThreads) {
-    const int64_t p0 = pre[u], p1 = pre[u + 1];
-    int32_t w0 = -1, w1 = -1;
+  auto begin_of = [&](int32_t w) -> int64_t {
+    if (narrow) return (int64_t)((uint32_t)w * (uint32_t)T / (uint32_t)P);
+    return worker_begin(T, P, w);
+  };
+  for (int32_t w = tid; w <= P; w += kSchedThreads) wbeg[w] = (int32_t)begin_of(w);
+  // who writes each unit; units cut by worker boundaries or without pages go to `fin`
+  auto place = [&](int64_t u, int64_t p0, int64_t p1) {
+    int32_t w0 = -1, w1 = -1, slot0 = -1;
     if (p1 > p0) {
       w0 = owner(p0);
       w1 = owner(p1 - 1);
-      if (w0 == w1) continue;  // written whole by its worker
+      // the unit is w0's first segment unless w0's range began before it
+      slot0 = piece_slot(w0, !(begin_of(w0) < p0));
     }
+    *(i32x4*)(usrc + 4 * u) = i32x4{w0, w1, slot0, 0};
+    if (p1 > p0 && w0 == w1) return;  // written whole by its worker
     const int32_t k = atomicAdd(&fin_count, 1);
     *(i32x4*)(fin + 4 * (int64_t)k) = i32x4{(int32_t)u, w0, w1, 0};
+  };
+  if (U <= pass) {
+    // one pass: the offsets are still in registers
+#pragma unroll
+    for (int k = 0; k < kSchedPer; ++k) {
+      const int64_t u = (int64_t)tid * per + k;
+      if (k < per && u < U) place(u, p0s[k], (int64_t)p0s[k] + cnts[k]);
+    }
+  } else {
+    __syncthreads();  // pre[] is complete and visible to the workgroup
+    for (int64_t u = tid; u < U; u += kSchedThreads) place(u, pre[u], pre[u + 1]);
   }
   __syncthreads();
   if (tid == 0) {
@@ -149,9 +188,11 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
 hipError_t launch_schedule(const int32_t* bounds, int32_t B, int32_t S, int32_t units_per_bs,
                            int32_t P, int32_t* fin, int32_t bs, int32_t max_blocks,
                            int32_t* ubounds, int32_t* pre, int32_t* flags, int32_t Tq,
-                           int32_t* qend, int32_t* redo, hipStream_t stream) {
+                           int32_t* qend, int32_t* redo, int32_t* usrc, int32_t* wbeg,
+                           hipStream_t stream) {
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, bounds, B, S,
-                     units_per_bs, P, fin, bs, max_blocks, ubounds, pre, flags, Tq, qend, redo);
+                     units_per_bs, P, fin, bs, max_blocks, ubounds, pre, flags, Tq, qend, redo,
+                     usrc, wbeg);
   return hipGetLastError();
 }
 
@@ -310,6 +351,147 @@ hipError_t launch_merge(int32_t B, int32_t S, int32_t H, int32_t Dv, const float
   int32_t grid = (int32_t)((n + 255) / 256);
   hipLaunchKernelGGL(merge_kernel, dim3(grid), dim3(256), 0, stream, B, S, H, Dv, part_o,
                      part_lse, out, out_lse);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- combine (fused calls)
+
+// out[b, rho, :] and out_lse[b, rho] of the fused calls straight from the attention kernel's
+// outputs, without the finishing pass: for each shard, the unit holding query row rho
+// contributes its partial row when one worker wrote it whole, the rows of its pieces when
+// worker boundaries cut it (one per covering worker whose range is not empty), and nothing
+// when it has no pages. All of them enter one LSE merge, which is associative: the result is
+// that of merging the pieces into each shard's partial and the partials into the output, up
+// to rounding order. kSplit consecutive threads share one output float4: thread t takes the
+// shards s = t (mod kSplit) and, of each cut unit, the pieces j = t (mod kSplit), and the
+// group's partial merges are combined across its lanes at the end (the same formula). A
+// thread issues its sources' loads kB at a time. kSplit > 1 serves launches with few output
+// values and many pieces per value, which one thread per value would walk through one memory
+// latency per batch.
+template <int kSplit, int kB>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+combine_kernel(AttnArgs a, float* __restrict__ out, float* __restrict__ out_lse) {
+  const int32_t dv4 = a.Dv >> 2;
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int32_t t = (int32_t)(q % kSplit);
+  const int64_t q4 = q / kSplit;
+  // the groups' lanes stay together to the end (kSplit divides the wave): no early exit
+  const bool live = q4 < (int64_t)a.B * a.R * dv4;
+  const int64_t br = live ? q4 / dv4 : 0;  // b * R + rho
+  const int32_t c4 = live ? (int32_t)(q4 - br * dv4) : 0;
+  const int32_t b = (int32_t)(br / a.R), rho = (int32_t)(br - (int64_t)b * a.R);
+  // the unit column and local row of query row rho = j Hq + kvh G + g (inverse of unit_row)
+  const int32_t jq = rho / a.Hq, hq = rho - jq * a.Hq;
+  const int32_t kvh = hq / a.G;
+  const int32_t rr = jq * a.G + (hq - kvh * a.G);
+  const int32_t rg = rr / a.Ru, h = rr - rg * a.Ru;
+  const int32_t per_bs = a.U / (a.B * a.S);
+  const int64_t col = (int64_t)kvh * a.NRg + rg;
+  const i32x4* usrc = (const i32x4*)a.usrc;
+  // with at least as many pages as workers no worker's range is empty
+  const bool all_ranges = a.pre[a.U] >= a.P;
+  float m = kNegInf, den = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // one batch of sources: the running max moves to the batch's max and the sums so far are
+  // rescaled by exp(m_old - m_new); a zero weight takes no part, whatever its O holds
+  auto merge = [&](const float* l, const f32x4* o) {
+    float mb = m;
+#pragma unroll
+    for (int c = 0; c < kB; ++c) mb = fmaxf(mb, l[c]);
+    const float sc = safe_exp_diff(m, mb);
+    den *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int c = 0; c < kB; ++c) {
+      const float wt = safe_exp_diff(l[c], mb);
+      den += wt;
+      if (wt != 0.f) acc += wt * o[c];
+    }
+    m = mb;
+  };
+  for (int32_t s0 = 0; live && s0 < a.S; s0 += kB) {
+    i32x4 src[kB];
+#pragma unroll
+    for (int c = 0; c < kB; ++c)
+      src[c] = s0 + c < a.S ? usrc[((int64_t)b * a.S + s0 + c) * per_bs + col]
+                            : i32x4{-1, -1, -1, 0};
+    // units written whole: their partial rows. The rows are loaded alongside the table (the
+    // workspace rows of the other units hold whatever an earlier call left) and weighted
+    // only where the table says one worker wrote the unit.
+    float l[kB];
+    f32x4 o[kB];
+#pragma unroll
+    for (int c = 0; c < kB; ++c) {
+      l[c] = kNegInf;
+      o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (s0 + c < a.S && (s0 + c) % kSplit == t) {
+        const int64_t row = ((int64_t)b * a.S + s0 + c) * a.R + rho;
+        l[c] = a.part_lse[row];
+        o[c] = *(const f32x4*)(a.part_o + row * a.Dv + 4 * c4);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kB; ++c)
+      if (!(src[c][0] >= 0 && src[c][0] == src[c][1])) l[c] = kNegInf;
+    merge(l, o);
+    // units cut by worker boundaries: their pieces
+#pragma unroll
+    for (int c = 0; c < kB; ++c) {
+      const int32_t w0 = src[c][0], w1 = src[c][1];
+      if (w0 < 0 || w0 == w1) continue;
+      for (int32_t k0 = w0 + t; k0 <= w1; k0 += kB * kSplit) {
+#pragma unroll
+        for (int k = 0; k < kB; ++k) {
+          const int32_t w = k0 + k * kSplit;
+          l[k] = kNegInf;
+          o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+          // the unit is the first segment of every covering worker but w0, whose slot the
+          // schedule recorded; a worker whose range is empty wrote nothing
+          if (w <= w1 && (all_ranges || w == w0 || a.wbeg[w + 1] > a.wbeg[w])) {
+            const int64_t sl = w == w0 ? src[c][2] : piece_slot(w, true);
+            l[k] = a.piece_lse[sl * a.Ru + h];
+            o[k] = *(const f32x4*)(a.piece_o + (sl * a.Ru + h) * a.Dv + 4 * c4);
+          }
+        }
+        merge(l, o);
+      }
+    }
+  }
+  // the group's partial merges, combined across its lanes
+#pragma unroll
+  for (int off = 1; off < kSplit; off <<= 1) {
+    const float m2 = __shfl_xor(m, off, 64);
+    const float d2 = __shfl_xor(den, off, 64);
+    f32x4 a2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a2[e] = __shfl_xor(acc[e], off, 64);
+    const float mb = fmaxf(m, m2);
+    const float s1 = safe_exp_diff(m, mb), s2 = safe_exp_diff(m2, mb);
+    den = den * s1 + d2 * s2;
+    acc = (s1 != 0.f ? acc * s1 : f32x4{0.f, 0.f, 0.f, 0.f}) +
+          (s2 != 0.f ? a2 * s2 : f32x4{0.f, 0.f, 0.f, 0.f});
+    m = mb;
+  }
+  if (!live || t != 0) return;
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  *(f32x4*)(out + br * a.Dv + 4 * c4) = acc * inv;
+  if (out_lse && c4 == 0) out_lse[br] = den > 0.f ? m + logf(den) : kNegInf;
+}
+
+hipError_t launch_combine(const AttnArgs& a, float* out, float* out_lse, hipStream_t stream) {
+  const int64_t n = (int64_t)a.B * a.R * (a.Dv / 4);
+  if (n == 0) return hipSuccess;
+  // few output values: eight threads per value, so that the launch has about as many
+  // threads as the one-per-value launch of a large batch
+  if (n < (int64_t)1 << 19) {
+    const int32_t grid = (int32_t)((8 * n + 255) / 256);
+    hipLaunchKernelGGL((combine_kernel<8, 2>), dim3(grid), dim3(256), 0, stream, a, out,
+                       out_lse);
+  } else {
+    const int32_t grid = (int32_t)((n + 255) / 256);
+    hipLaunchKernelGGL((combine_kernel<1, 8>), dim3(grid), dim3(256), 0, stream, a, out,
+                       out_lse);
+  }
   return hipGetLastError();
 }
 
