@@ -173,7 +173,6 @@ dcp_status make_plan(const dcp_attn_shape* sh, int32_t Tq, dcp::Plan* plan) {
   w.qend = off;        off = align_up(off + sizeof(int32_t) * B);
   w.redo = off;        off = align_up(off + sizeof(int32_t) * (size_t)pmax);
   w.usrc = off;        off = align_up(off + sizeof(int32_t) * 4 * (size_t)units);
-  w.wbeg = off;        off = align_up(off + sizeof(int32_t) * ((size_t)pmax + 1));
   w.piece_o = off;     off = align_up(off + sizeof(float) * 2 * (size_t)pmax * ru * Dv);
   w.piece_lse = off;   off = align_up(off + sizeof(float) * 2 * (size_t)pmax * ru);
   w.part_o = off;      off = align_up(off + sizeof(float) * B * S * R * Dv);
@@ -222,7 +221,6 @@ dcp_status run_partials(const dcp_attn_shape* sh, int32_t Tq, const void* q, con
   a.pre = reinterpret_cast<int32_t*>(ws + plan.ws.pre);
   a.fin = reinterpret_cast<int32_t*>(ws + plan.ws.fin);
   a.usrc = reinterpret_cast<int32_t*>(ws + plan.ws.usrc);
-  a.wbeg = reinterpret_cast<int32_t*>(ws + plan.ws.wbeg);
   a.qend = reinterpret_cast<int32_t*>(ws + plan.ws.qend);
   a.redo = reinterpret_cast<int32_t*>(ws + plan.ws.redo);
   a.part_o = fused ? reinterpret_cast<float*>(ws + plan.ws.part_o) : part_o;
@@ -260,7 +258,7 @@ dcp_status run_partials(const dcp_attn_shape* sh, int32_t Tq, const void* q, con
                            reinterpret_cast<int32_t*>(ws + plan.ws.fin), a.bs, a.max_blocks,
                            const_cast<int32_t*>(a.ubounds), const_cast<int32_t*>(a.pre), a.flags,
                            Tq, const_cast<int32_t*>(a.qend), a.redo,
-                           const_cast<int32_t*>(a.usrc), const_cast<int32_t*>(a.wbeg), s);
+                           const_cast<int32_t*>(a.usrc), s);
   if (e != hipSuccess) return device_fail(e, "schedule launch");
   const bool timed = g_timing.on && g_timing.used < g_timing.start.size();
   if (timed) {

@@ -45,18 +45,16 @@ constexpr int32_t kFlagRescaled = 8;    // a worker raised a row's reference and
 //   ubounds    int32[B*S*2]      sanitised (start, end) per (request, shard)
 //   qend       int32[B]          position of each request's first query token
 //   redo       int32[Pmax]       workers a kernel marked for recomputation
-//   usrc       int32[U][4]       per unit, who wrote it: (w, w, -, 0) for a unit written whole
-//                                by worker w, (first worker, last worker, piece slot of the
-//                                first, 0) for a unit cut by worker boundaries, (-1, -1, -1, 0)
-//                                for a unit with no pages
-//   wbeg       int32[Pmax + 1]   first page of each worker's range, wbeg[P] = T
+//   usrc       int32[U][4]       per unit, who wrote it: (first worker, last worker, piece slot
+//                                of the first, first page); the two workers are equal for a
+//                                unit written whole, -1 for a unit with no pages
 //   piece_o    float[2*Pmax][Ru][Dv]
 //   piece_lse  float[2*Pmax][Ru]
 //   part_o     float[B][S][R][Dv]    (fused path only)
 //   part_lse   float[B][S][R]
 struct WsLayout {
-  size_t flags, pre, fin, ubounds, qend, redo, usrc, wbeg, piece_o, piece_lse, part_o,
-      part_lse, total;
+  size_t flags, pre, fin, ubounds, qend, redo, usrc, piece_o, piece_lse, part_o, part_lse,
+      total;
 };
 
 enum class Kernel { kNone = 0, kGqaValu, kGqaMfma, kGqaChunk, kMlaMfma };
@@ -80,7 +78,6 @@ struct AttnArgs {
   const int32_t* pre;       // [U + 1]
   const int32_t* fin;       // [U][4], count in flags[1]
   const int32_t* usrc;      // [U][4] writers of each unit
-  const int32_t* wbeg;      // [P + 1] worker range starts
   const int32_t* qend;      // [B]
   float* part_o;            // [B][S][R][Dv]
   float* part_lse;          // [B][S][R]
@@ -111,7 +108,7 @@ hipError_t launch_schedule(const int32_t* bounds, int32_t B, int32_t S, int32_t 
                            int32_t P, int32_t* fin,
                            int32_t bs, int32_t max_blocks, int32_t* ubounds, int32_t* pre,
                            int32_t* flags, int32_t Tq, int32_t* qend, int32_t* redo,
-                           int32_t* usrc, int32_t* wbeg, hipStream_t stream);
+                           int32_t* usrc, hipStream_t stream);
 hipError_t launch_finish_units(const AttnArgs& a, hipStream_t stream);
 // out / out_lse straight from the pieces and partials (fused calls; no finishing pass)
 hipError_t launch_combine(const AttnArgs& a, float* out, float* out_lse, hipStream_t stream);

@@ -37,8 +37,8 @@ hipError_t launch_plan_device(const int32_t* seq_lens, int32_t B, int32_t S, int
 // One workgroup: sanitise the bounds of every (request, shard), count each unit's pages and
 // write the exclusive prefix sum pre[0..U] (units ordered (b, s, h) with h < units_per_bs).
 // A second pass lists the units the finishing pass must write (cut by a worker boundary, or
-// without pages) in `fin`, with their count in flags[1], records who wrote each unit in
-// `usrc` and each worker's first page in `wbeg` (for the combining pass). Also clears the
+// without pages) in `fin`, with their count in flags[1], and records who wrote each unit in
+// `usrc` (for the combining pass). Also clears the
 // flag word (the first call of a step owns it) and the P recomputation marks.
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedPer = 4;  // consecutive units per thread in one pass of the scan
@@ -48,8 +48,7 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
                 int32_t P, int32_t* __restrict__ fin, int32_t bs, int32_t max_blocks,
                 int32_t* __restrict__ ubounds, int32_t* __restrict__ pre,
                 int32_t* __restrict__ flags, int32_t Tq, int32_t* __restrict__ qend,
-                int32_t* __restrict__ redo, int32_t* __restrict__ usrc,
-                int32_t* __restrict__ wbeg) {
+                int32_t* __restrict__ redo, int32_t* __restrict__ usrc) {
   __shared__ int32_t warp_sums[kSchedThreads / 64];
   __shared__ int32_t carry;
   __shared__ int32_t flag_acc;
@@ -152,7 +151,6 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
     if (narrow) return (int64_t)((uint32_t)w * (uint32_t)T / (uint32_t)P);
     return worker_begin(T, P, w);
   };
-  for (int32_t w = tid; w <= P; w += kSchedThreads) wbeg[w] = (int32_t)begin_of(w);
   // who writes each unit; units cut by worker boundaries or without pages go to `fin`
   auto place = [&](int64_t u, int64_t p0, int64_t p1) {
     int32_t w0 = -1, w1 = -1, slot0 = -1;
@@ -162,7 +160,7 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
       // the unit is w0's first segment unless w0's range began before it
       slot0 = piece_slot(w0, !(begin_of(w0) < p0));
     }
-    *(i32x4*)(usrc + 4 * u) = i32x4{w0, w1, slot0, 0};
+    *(i32x4*)(usrc + 4 * u) = i32x4{w0, w1, slot0, (int32_t)p0};
     if (p1 > p0 && w0 == w1) return;  // written whole by its worker
     const int32_t k = atomicAdd(&fin_count, 1);
     *(i32x4*)(fin + 4 * (int64_t)k) = i32x4{(int32_t)u, w0, w1, 0};
@@ -188,11 +186,10 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
 hipError_t launch_schedule(const int32_t* bounds, int32_t B, int32_t S, int32_t units_per_bs,
                            int32_t P, int32_t* fin, int32_t bs, int32_t max_blocks,
                            int32_t* ubounds, int32_t* pre, int32_t* flags, int32_t Tq,
-                           int32_t* qend, int32_t* redo, int32_t* usrc, int32_t* wbeg,
-                           hipStream_t stream) {
+                           int32_t* qend, int32_t* redo, int32_t* usrc, hipStream_t stream) {
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, bounds, B, S,
                      units_per_bs, P, fin, bs, max_blocks, ubounds, pre, flags, Tq, qend, redo,
-                     usrc, wbeg);
+                     usrc);
   return hipGetLastError();
 }
 
@@ -388,8 +385,10 @@ combine_kernel(AttnArgs a, float* __restrict__ out, float* __restrict__ out_lse)
   const int32_t per_bs = a.U / (a.B * a.S);
   const int64_t col = (int64_t)kvh * a.NRg + rg;
   const i32x4* usrc = (const i32x4*)a.usrc;
-  // with at least as many pages as workers no worker's range is empty
-  const bool all_ranges = a.pre[a.U] >= a.P;
+  // with at least as many pages as workers no worker's range is empty; with fewer, each
+  // worker's range holds at most one page, and the pieces of a unit are its pages' owners
+  const int64_t T = a.pre[a.U];
+  const bool all_ranges = T >= a.P;
   float m = kNegInf, den = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   // one batch of sources: the running max moves to the batch's max and the sums so far are
@@ -439,16 +438,20 @@ combine_kernel(AttnArgs a, float* __restrict__ out, float* __restrict__ out_lse)
     for (int c = 0; c < kB; ++c) {
       const int32_t w0 = src[c][0], w1 = src[c][1];
       if (w0 < 0 || w0 == w1) continue;
-      for (int32_t k0 = w0 + t; k0 <= w1; k0 += kB * kSplit) {
+      // pieces j = 0 .. n - 1: the covering workers in order, or the unit's pages' owners
+      const int64_t p0 = src[c][3];
+      const int32_t n = all_ranges ? w1 - w0 + 1 : (int32_t)((int64_t)w1 * T / a.P + 1 - p0);
+      for (int32_t j0 = t; j0 < n; j0 += kB * kSplit) {
 #pragma unroll
         for (int k = 0; k < kB; ++k) {
-          const int32_t w = k0 + k * kSplit;
+          const int32_t jj = j0 + k * kSplit;
           l[k] = kNegInf;
           o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-          // the unit is the first segment of every covering worker but w0, whose slot the
-          // schedule recorded; a worker whose range is empty wrote nothing
-          if (w <= w1 && (all_ranges || w == w0 || a.wbeg[w + 1] > a.wbeg[w])) {
-            const int64_t sl = w == w0 ? src[c][2] : piece_slot(w, true);
+          if (jj < n) {
+            // the unit is the first segment of every covering worker but w0, whose slot the
+            // schedule recorded
+            const int32_t w = all_ranges || jj == 0 ? w0 + jj : worker_of(T, a.P, p0 + jj);
+            const int64_t sl = jj == 0 ? src[c][2] : piece_slot(w, true);
             l[k] = a.piece_lse[sl * a.Ru + h];
             o[k] = *(const f32x4*)(a.piece_o + (sl * a.Ru + h) * a.Dv + 4 * c4);
           }
