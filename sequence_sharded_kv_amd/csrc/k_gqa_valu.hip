@@ -4,13 +4,15 @@
 // Each wave is one stream-K worker. Per 64-token tile, lane t scores token t against the G
 // query heads of its KV head (q broadcast from LDS), the per-head tile max and the running
 // sums use wave shuffles, and the P.V product switches to lanes-over-dims: the tile's
-// probabilities go through LDS and every lane accumulates its dims of O over the 64 tokens.
+// probabilities go through LDS and every lane accumulates its dims of O over the 64 tokens,
+// with each token's V row address taken from the lane that looked up its page.
 #include "device_common.h"
 
 namespace dcp {
 
 constexpr int kValuWaves = 2;  // keeps dynamic LDS <= 40 KB
 constexpr int kValuMaxG = 16;
+constexpr int kValuVBatch = 4;  // V rows whose loads are in flight together
 
 template <typename T>
 struct Elem;
@@ -24,6 +26,25 @@ struct Elem<uint16_t> {
     return bf16_bits_to_f32(p[i]);
   }
 };
+
+// Eight consecutive elements from p + i (i a multiple of 8, p 16-byte aligned) with 128-bit
+// loads.
+__device__ __forceinline__ void load8(const float* p, int64_t i, float* out) {
+  const f32x4 a0 = *(const f32x4*)(p + i), a1 = *(const f32x4*)(p + i + 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    out[j] = a0[j];
+    out[4 + j] = a1[j];
+  }
+}
+__device__ __forceinline__ void load8(const uint16_t* p, int64_t i, float* out) {
+  const u32x4 w = *(const u32x4*)(p + i);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    out[2 * j] = __uint_as_float(w[j] << 16);
+    out[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+  }
+}
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -112,8 +133,7 @@ gqa_valu_kernel(AttnArgs a) {
       if (valid) {
         for (int d = 0; d < D; d += 8) {
           float kv[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) kv[j] = Elem<T>::get(K, row + d + j);
+          load8(K, row + d, kv);
 #pragma unroll
           for (int h = 0; h < kValuMaxG; ++h) {
             if (h < Ru) {
@@ -139,20 +159,33 @@ gqa_valu_kernel(AttnArgs a) {
         }
       }
       __builtin_amdgcn_wave_barrier();
-      for (int tt = 0; tt < nvalid; ++tt) {
-        const int64_t tv = tile + tt;
-        int32_t blk = brow[tv / a.bs];
-        if (blk < 0 || blk >= a.num_blocks) continue;
-        const int64_t vrow = (((int64_t)blk * a.Hkv + kvh) * a.bs + tv % a.bs) * D;
-        float vv[NDV];
+      // V rows of the tile's tokens, kValuVBatch at a time: token tt's row (K and V share the
+      // cache layout) comes from lane tt, so no table load sits in this loop, and the batch's
+      // loads are in flight together; tokens without a valid row are skipped (their weight is
+      // zero, and their row may hold anything)
+      const uint64_t vmask = __ballot(valid);
+      for (int tt0 = 0; tt0 < nvalid; tt0 += kValuVBatch) {
+        float vv[kValuVBatch][NDV];
 #pragma unroll
-        for (int j = 0; j < NDV; ++j) vv[j] = Elem<T>::get(V, vrow + lane + 64 * j);
+        for (int k = 0; k < kValuVBatch; ++k) {
+          const int tt = tt0 + k;  // wave-uniform
+          const bool use = tt < nvalid && ((vmask >> tt) & 1u);
+          const int64_t vrow = (int64_t)readlane_u64((uint64_t)row, tt < 64 ? tt : 0);
 #pragma unroll
-        for (int h = 0; h < kValuMaxG; ++h) {
-          if (h < Ru) {
-            float p = ps[h * 64 + tt];
+          for (int j = 0; j < NDV; ++j)
+            vv[k][j] = use ? Elem<T>::get(V, vrow + lane + 64 * j) : 0.f;
+        }
 #pragma unroll
-            for (int j = 0; j < NDV; ++j) acc[h][j] = fmaf(p, vv[j], acc[h][j]);
+        for (int k = 0; k < kValuVBatch; ++k) {
+          const int tt = tt0 + k;
+          if (tt >= nvalid) break;
+#pragma unroll
+          for (int h = 0; h < kValuMaxG; ++h) {
+            if (h < Ru) {
+              const float p = ps[h * 64 + tt];
+#pragma unroll
+              for (int j = 0; j < NDV; ++j) acc[h][j] = fmaf(p, vv[k][j], acc[h][j]);
+            }
           }
         }
       }
