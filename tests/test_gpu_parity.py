@@ -42,6 +42,13 @@ CASES = [
     ("mla-64h-bs1", "mla-64h-b512", [200, 33], dict(batch=2, block_size=1)),
     ("gqa-g16-bs24", "gqa-g16", [500, 49], dict(batch=2, block_size=24)),
     ("mla-64h-bs48", "mla-64h-b512", [700, 97], dict(batch=2, block_size=48)),
+    # output sizes that take the combine pass's one-thread-per-value instance (64 requests x
+    # 64 heads x 512 dims): 16 shards (two batches of shards), and fewer pages than workers
+    # (the pieces of a unit found through its pages' owners)
+    ("mla-64h-b64-S16", "mla-64h-b512", [100 + 13 * i for i in range(64)],
+     dict(batch=64, num_shards=16)),
+    ("mla-64h-b64-few-pages", "mla-64h-b512", [20 + (7 * i) % 41 for i in range(64)],
+     dict(batch=64, block_size=16, num_shards=2)),
 ]
 
 
