@@ -23,6 +23,8 @@
 // (i % 16) ^ sw(row)).
 #include "device_common.h"
 
+#include <type_traits>
+
 namespace dcp {
 
 namespace gchunk {
@@ -64,17 +66,36 @@ gqa_chunk_kernel(AttnArgs a) {
   if (g0 >= g1) return;
   int32_t u = find_unit(a.pre, a.U, g0);
   int64_t gg = g0;
-  int32_t bad = 0;
+  int32_t bad = 0, raised = 0;
   const bool bs_pow2 = (a.bs & (a.bs - 1)) == 0;
   const int bs_shift = __builtin_ctz((unsigned)a.bs);
   const uint32_t lds0 = lds_u32(&lds[0]);
 
-  // transposed value reads: 16-lane group q4, lane L reads rows 16 kk + 4 (q4 >> 1) + (L >> 2)
-  // and + 8, chunk 4 mt + 2 (q4 & 1) + ((L & 3) >> 1), byte 8 (L & 1) of the chunk
-  const int q4 = lane >> 4, L = lane & 15;
-  const int vr = 4 * (q4 >> 1) + (L >> 2);
-  const int vc = 2 * (q4 & 1) + ((L & 3) >> 1);
-  const int vw = 8 * (L & 1);
+  // Per-lane LDS byte offsets within a slot, fixed for the kernel; a slot's base and the
+  // value product's second 16-token k step (16 rows = 4096 B further) are immediates.
+  //   score reads: row c32, chunk (2 ks + g) ^ sw(c32);
+  //   transposed value reads: 16-lane group q4, lane L reads rows 4 (q4 >> 1) + (L >> 2) (+ 8),
+  //   chunk 4 mt + 2 (q4 & 1) + ((L & 3) >> 1), byte 8 (L & 1) of the chunk. sw(r) depends on
+  //   r mod 16 only.
+  uint32_t koff[8], voff[8];
+  {
+    const int fq = sw(c32);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) koff[ks] = c32 * kRowB + 16 * ((2 * ks + g) ^ fq);
+    const int q4 = lane >> 4, L = lane & 15;
+    const int vr = 4 * (q4 >> 1) + (L >> 2);
+    const int vc = 2 * (q4 & 1) + ((L & 3) >> 1);
+    const int vw = 8 * (L & 1);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int r = vr + 8 * hf;
+        voff[2 * mt + hf] = kTileB + r * kRowB + vw + 16 * ((vc + 4 * mt) ^ sw(r));
+      }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) asm volatile("" : "+v"(koff[q]), "+v"(voff[q]));
+  }
 
   while (gg < g1) {
     while ((int64_t)a.pre[u + 1] <= gg) ++u;
@@ -115,45 +136,36 @@ gqa_chunk_kernel(AttnArgs a) {
     };
 
     // Queue tile i into slot i % kSlots: this wave's copy instructions k = wv + NW m of the K
-    // tile and of the V tile. Lane t < 32 first forms the byte offset of token tile + t's row
-    // (or marks it invalid); returns the tile's valid-token mask.
+    // tile and of the V tile. Lane t (and t + 32) finds token tile + t's row in the caches (-1
+    // for an invalid page) with one lane permute of the page ids; each copy lane then fetches
+    // the row index of its own row the same way. Returns the tile's valid-token mask.
     auto issue_tile = [&](int32_t i) -> uint32_t {
       const int32_t tile = t0i + 32 * i;
       const int32_t tl = (tile + 31 < t1i ? tile + 31 : t1i - 1);
-      const int32_t pfirst = page_idx(tile), plast = page_idx(tl);
-      ensure_pages(pfirst, plast);
+      ensure_pages(page_idx(tile), page_idx(tl));
       const int32_t t = tile + c32;
       const int32_t tc = t < t1i ? t : t1i - 1;
-      const int32_t mypage = page_idx(tc);
-      int32_t blk = -1;
-      for (int32_t pg = pfirst; pg <= plast; ++pg) {
-        const int32_t id = __builtin_amdgcn_readlane(pid, pg - pchunk);
-        blk = (mypage == pg) ? id : blk;
-      }
+      const int32_t blk = __builtin_amdgcn_ds_bpermute(4 * (page_idx(tc) - pchunk), pid);
       const bool page_ok = blk >= 0 && blk < a.num_blocks;
       const uint32_t slot = bs_pow2 ? (uint32_t)(tc & (a.bs - 1)) : (uint32_t)(tc % a.bs);
-      const uint32_t row = ((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)kvh) * (uint32_t)a.bs + slot;
-      // byte offset of the row in the caches; -1 sends the copy to the workspace's zero row
-      const int64_t off = page_ok ? (int64_t)row * kRowB : -1;
-      bad |= __any(lane < 32 && !page_ok) ? 1 : 0;
+      // row index in the caches (below 2^32 - 1 for any pool that fits in device memory), all
+      // ones for an invalid page
+      const uint32_t row =
+          page_ok ? ((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)kvh) * (uint32_t)a.bs + slot
+                  : 0xFFFFFFFFu;
+      bad |= __any(!page_ok) ? 1 : 0;
       const uint32_t mask = (uint32_t)__ballot(lane < 32 && page_ok && t < t1i);
       const uint32_t base = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((i % kSlots) * kSlotB));
       const int sub = lane >> 4, p = lane & 15;
 #pragma unroll
       for (int m = 0; m < 8 / NW; ++m) {
         const int k = wv + NW * m;  // rows 4k .. 4k + 3
-        int64_t ro = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int32_t lo = __builtin_amdgcn_readlane((uint32_t)off, 4 * k + e);
-          const int32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)off >> 32), 4 * k + e);
-          const int64_t oe = (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-          ro = (sub == e) ? oe : ro;
-        }
         const int r = 4 * k + sub;
+        const uint32_t rr = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * r, (int)row);
         const int64_t chunk = 16 * (p ^ sw(r));
-        const char* ks = ro >= 0 ? Kc + ro + chunk : a.zero_row + chunk;
-        const char* vs = ro >= 0 ? Vc + ro + chunk : a.zero_row + chunk;
+        const bool ok = rr != 0xFFFFFFFFu;
+        const char* ks = ok ? Kc + (uint64_t)rr * kRowB + chunk : a.zero_row + chunk;
+        const char* vs = ok ? Vc + (uint64_t)rr * kRowB + chunk : a.zero_row + chunk;
         dma16(ks, base + k * 1024);
         dma16(vs, base + kTileB + k * 1024);
       }
@@ -185,7 +197,13 @@ gqa_chunk_kernel(AttnArgs a) {
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
-    float m_run = kNegInf, l_run = 0.f;
+    // Reference max: the row's weights are exp2(s - m_ref) with m_ref set by the first tile
+    // where the row sees a token (its sum and accumulator are still zero then) and raised only
+    // when a later tile's maximum exceeds it by kLazy, which rescales the row's sum and
+    // accumulator; otherwise the weights stay below 2^kLazy and nothing is rescaled.
+    constexpr float kLazy = 16.f;
+    float m_ref = kNegInf, l_run = 0.f;
+    const float sl2 = a.scale_log2;
 
     uint32_t maskv = 0;  // lane s: valid-token mask of the tile in slot s
     int32_t issued = 0;
@@ -198,90 +216,108 @@ gqa_chunk_kernel(AttnArgs a) {
     wait_tiles(issued - 1);
     __syncthreads();
 
-    for (int32_t i = 0; i < ntiles; ++i) {
+    // one tile in slot S (a compile-time constant: the LDS offsets are immediates)
+    auto body = [&](auto slot_tag, int32_t i) {
+      constexpr int S = decltype(slot_tag)::value;
       if (issued < ntiles) {
         const uint32_t m = issue_tile(issued);
         maskv = (lane == issued % kSlots) ? m : maskv;
         ++issued;
       }
       const int32_t tile = t0i + 32 * i;
-      const char* tk = &lds[(i % kSlots) * kSlotB];
-      const char* tv = tk + kTileB;
       const int32_t dl = lim - tile;
-      const uint32_t mask = __builtin_amdgcn_readlane(maskv, i % kSlots) &
+      const uint32_t mask = __builtin_amdgcn_readlane(maskv, S) &
                             (dl < 0 ? 0u : dl >= 31 ? 0xFFFFFFFFu : (2u << dl) - 1u);
+      const bool full = __ballot(mask != 0xFFFFFFFFu) == 0;  // wave-uniform
+      const char* tb = lds + S * kSlotB;
 
       // S[32 tok x 32 rows] = K . Q^T
-      int fq = sw(c32);
-      asm volatile("" : "+v"(fq));
-      const char* krow = tk + c32 * kRowB;
       f32x16 st;
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[r] = 0.f;
       bf16x8 kbuf[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        kbuf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(krow + 16 * ((2 * ks + g) ^ fq)));
+      for (int ks = 0; ks < 4; ++ks) kbuf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(tb + koff[ks]));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const bf16x8 kop = kbuf[ks & 3];
         if (ks + 4 < 8)
-          kbuf[ks & 3] = __builtin_bit_cast(
-              bf16x8, *(const u32x4*)(krow + 16 * ((2 * (ks + 4) + g) ^ fq)));
+          kbuf[ks & 3] = __builtin_bit_cast(bf16x8, *(const u32x4*)(tb + koff[ks + 4]));
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], st, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // online softmax of row c32; st[r] is token 8 (r / 4) + 4 g + r % 4
-      float x[16];
-      float tmax = kNegInf;
+      // row c32's maximum over the tile; st[r] is token 8 (r / 4) + 4 g + r % 4
       const uint32_t hmask = mask >> (4 * g);
+      auto valid = [&](int r) { return ((hmask >> (8 * (r >> 2) + (r & 3))) & 1u) != 0u; };
+      float tmax = kNegInf;
+      if (full) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        x[r] = ((hmask >> (8 * (r >> 2) + (r & 3))) & 1u) ? st[r] * a.scale_log2 : kNegInf;
-        tmax = fmaxf(tmax, x[r]);
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, valid(r) ? st[r] : kNegInf);
       }
       {
         auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
                                                    false, false);
         tmax = fmaxf(__uint_as_float(s2[0]), __uint_as_float(s2[1]));
       }
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
-      if (!__all(alpha == 1.f)) {
+      const float tm = tmax * sl2;  // the scaled maximum (scaling is monotonic)
+      float rs = 1.f;
+      if (m_ref == kNegInf) {
+        m_ref = tm;
+      } else if (tm > m_ref + kLazy) {
+        rs = fast_exp2(m_ref - tm);
+        m_ref = tm;
+      }
+      if (__ballot(rs != 1.f) != 0) {
+        raised = 1;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt] *= alpha;
+        for (int mt = 0; mt < 4; ++mt) acc[mt] *= rs;
+        l_run *= rs;
+      }
+      const float nm = -m_ref;
+      float pv[16];
+      if (full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(__builtin_fmaf(st[r], sl2, nm));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          pv[r] = valid(r) ? fast_exp2(__builtin_fmaf(st[r], sl2, nm)) : 0.f;
       }
       float psum = 0.f;
       bf16x8 phi[2], plo[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = (x[r] == kNegInf) ? 0.f : fast_exp2(x[r] - m_new);
-        psum += pv;
-        const __bf16 hi = (__bf16)pv;
+        psum += pv[r];
+        const __bf16 hi = (__bf16)pv[r];
         phi[r >> 3][r & 7] = hi;
-        plo[r >> 3][r & 7] = (__bf16)(pv - (float)hi);
+        plo[r >> 3][r & 7] = (__bf16)(pv[r] - (float)hi);
       }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+      l_run += psum;
 
       // O^T[128 x 32 rows] += V^T . P over two 16-token k steps
-      int vcq = vc;
-      asm volatile("" : "+v"(vcq));
 #pragma unroll
       for (int s2 = 0; s2 < 8; ++s2) {
         const int kk = s2 >> 2, mt = s2 & 3;
-        const int r1 = 16 * kk + vr;
-        const bf16x8 vop =
-            tr_pair(tv + r1 * kRowB + vw + 16 * ((vcq + 4 * mt) ^ sw(r1)),
-                    tv + (r1 + 8) * kRowB + vw + 16 * ((vcq + 4 * mt) ^ sw(r1 + 8)));
+        const bf16x8 vop = tr_pair(tb + 4096 * kk + voff[2 * mt], tb + 4096 * kk + voff[2 * mt + 1]);
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, phi[kk], acc[mt], 0, 0, 0);
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, plo[kk], acc[mt], 0, 0, 0);
       }
       // tile i + 1 has landed and every wave is past tile i (its slot is refilled next)
       wait_tiles(issued - (i + 2));
       __syncthreads();
+    };
+    for (int32_t i = 0; i < ntiles;) {
+      body(std::integral_constant<int, 0>{}, i);
+      if (++i >= ntiles) break;
+      body(std::integral_constant<int, 1>{}, i);
+      if (++i >= ntiles) break;
+      body(std::integral_constant<int, 2>{}, i);
+      ++i;
     }
 
     // finalise: l over the two lanes of row c32
@@ -310,11 +346,12 @@ gqa_chunk_kernel(AttnArgs a) {
           *(f32x4*)(dst_o + 32 * mt + 8 * r4 + 4 * g) =
               f32x4{acc[mt][4 * r4], acc[mt][4 * r4 + 1], acc[mt][4 * r4 + 2],
                     acc[mt][4 * r4 + 3]} * inv;
-      if (g == 0) *dst_l = l > 0.f ? (m_run + fast_log2(l)) * kLn2 : kNegInf;
+      if (g == 0) *dst_l = l > 0.f ? (m_ref + fast_log2(l)) * kLn2 : kNegInf;
     }
     gg = sg1;
   }
   if (bad && lane == 0) atomicOr(a.flags, kFlagBadBlock);
+  if (__any(raised) && lane == 0) atomicOr(a.flags, kFlagRescaled);
 }
 
 int32_t gqa_chunk_workers(int device, int32_t Ru, int32_t max_workers) {

@@ -232,6 +232,58 @@ def test_lazy_max_mla_handles_scores_that_outrun_the_first_tile(wl_name):
     assert_close(out.cpu().numpy(), out_lse.cpu().numpy(), fo, fl, wl.dtype, "planted high score")
 
 
+def test_lazy_max_gqa_chunk_handles_scores_that_outrun_the_first_tile():
+    """The GQA chunk kernel also weights each row against its first-tile maximum. Keys
+    planted at four places in shard 1 of request 0 score about 90 (natural log units) above
+    the rest for one query row of a 48-token chunk: the workers that meet one past their first
+    tile raise that row's reference and rescale its sum and accumulator (flag bit 3), and the
+    partials and the fused result match the oracle."""
+    from workloads import bf16_bits_from_f32
+    say("[gpu] lazy-max GQA chunk kernel with planted high-score keys")
+    wl = workload("gqa-g16").replace(batch=2)
+    lengths = [3000, 1000]
+    T = 48
+    host = make_host_inputs(wl, lengths=lengths)
+    qh = make_queries(wl, T)
+    bs = wl.block_size
+    bounds_np = dcp.dcp_plan_shards(host["seq_lens"], wl.num_shards, bs)
+    # query token 5, head 3 (KV head 0) of request 0
+    qv = (qh[0, 5, 3].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    c = 90.0 / (wl.softmax_scale * float(qv @ qv))
+    key = bf16_bits_from_f32((c * qv).astype(np.float32))
+    start = int(bounds_np[0, 1, 0])
+    for k in range(4):
+        t = start + (10 + 20 * k) * bs + 5
+        assert t < lengths[0] - T
+        host["k_cache"][host["block_table"][0, t // bs], 0, t % bs] = key
+    inp = to_device(wl, host)
+    q = _q_device(wl, qh)
+    sh = shape_of(wl, inp)
+    B, S, Hq, Dv = wl.batch, wl.num_shards, wl.num_q_heads, wl.head_dim_v
+    bounds = torch.from_numpy(bounds_np).cuda()
+    ws = dcp.alloc_workspace(sh, "cuda", T)
+    po = torch.empty((B, S, T, Hq, Dv), dtype=torch.float32, device="cuda")
+    pl = torch.empty((B, S, T, Hq), dtype=torch.float32, device="cuda")
+    dcp.dcp_decode_attn_multi_partial(sh, T, q, inp["k_cache"], inp["v_cache"],
+                                      inp["block_table"], bounds, po, pl, ws)
+    out = torch.empty((B, T, Hq, Dv), dtype=torch.float32, device="cuda")
+    out_lse = torch.empty((B, T, Hq), dtype=torch.float32, device="cuda")
+    dcp.dcp_decode_attn_multi(sh, T, q, inp["k_cache"], inp["v_cache"], inp["block_table"],
+                              bounds, ws, out, out_lse)
+    torch.cuda.synchronize()
+    assert dcp.dcp_read_device_flags(ws) == 8
+    _, caches, bt, _ = host_inputs_of(wl, inp)
+    ro, rl = O.partial_attention_multi(wl.kind, wl.dtype, qh, caches, bt,
+                                       np.asarray(bounds_np, np.int64), bs, wl.softmax_scale, Dv)
+    assert float(np.max(rl[0, 1, 5, 3])) > 80.0
+    assert_close(po.cpu().numpy().reshape(B, S, T * Hq, Dv), pl.cpu().numpy().reshape(B, S, T * Hq),
+                 ro.reshape(B, S, T * Hq, Dv), rl.reshape(B, S, T * Hq), wl.dtype,
+                 "chunk planted partials")
+    fo, fl = O.merge_lse(ro.reshape(B, S, T * Hq, Dv), rl.reshape(B, S, T * Hq))
+    assert_close(out.cpu().numpy().reshape(B, T * Hq, Dv), out_lse.cpu().numpy().reshape(B, T * Hq),
+                 fo, fl, wl.dtype, "chunk planted fused")
+
+
 @pytest.mark.parametrize("case", ["huge-value", "tiny-values"])
 def test_fp16_value_kernel_recomputes_what_fp16_cannot_hold(case):
     """128 query rows per unit take the value product in fp16. A latent value of 70000
