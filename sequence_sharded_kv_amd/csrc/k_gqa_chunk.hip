@@ -248,16 +248,24 @@ gqa_chunk_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // row c32's maximum over the tile; st[r] is token 8 (r / 4) + 4 g + r % 4
-      const uint32_t hmask = mask >> (4 * g);
+      // row c32's maximum over the tile; st[r] is token 8 (r / 4) + 4 g + r % 4. A tile with
+      // every token visible skips the masks (their bits are formed inside the masked branch
+      // only).
+      uint32_t hmask = 0;
       auto valid = [&](int r) { return ((hmask >> (8 * (r >> 2) + (r & 3))) & 1u) != 0u; };
       float tmax = kNegInf;
       if (full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[r]);
       } else {
+        hmask = mask >> (4 * g);
+        asm volatile("" : "+v"(hmask));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, valid(r) ? st[r] : kNegInf);
+        for (int r = 0; r < 16; ++r) {
+          // a masked score becomes -inf here, so the weights below need no second mask
+          st[r] = valid(r) ? st[r] : kNegInf;
+          tmax = fmaxf(tmax, st[r]);
+        }
       }
       {
         auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
@@ -278,25 +286,30 @@ gqa_chunk_kernel(AttnArgs a) {
         for (int mt = 0; mt < 4; ++mt) acc[mt] *= rs;
         l_run *= rs;
       }
-      const float nm = -m_ref;
+      // Weights; a masked score is -inf and gives exp2(-inf) = 0, unless the row has seen no
+      // token yet (m_ref = -inf), where every score of the tile is masked and the weights are
+      // set to zero instead.
+      const float nm = m_ref == kNegInf ? 0.f : -m_ref;
       float pv[16];
-      if (full) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(__builtin_fmaf(st[r], sl2, nm));
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          pv[r] = valid(r) ? fast_exp2(__builtin_fmaf(st[r], sl2, nm)) : 0.f;
-      }
+      for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(__builtin_fmaf(st[r], sl2, nm));
+      // bf16 high parts packed in pairs; the remainders from the unpacked highs
       float psum = 0.f;
-      bf16x8 phi[2], plo[2];
+      u32x4 hpk[2], lpk[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        psum += pv[r];
-        const __bf16 hi = (__bf16)pv[r];
-        phi[r >> 3][r & 7] = hi;
-        plo[r >> 3][r & 7] = (__bf16)(pv[r] - (float)hi);
+      for (int q = 0; q < 8; ++q) {
+        const float p0 = pv[2 * q], p1 = pv[2 * q + 1];
+        psum += p0 + p1;
+        typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+        const bf16x2 h = {(__bf16)p0, (__bf16)p1};
+        const uint32_t hbits = __builtin_bit_cast(uint32_t, h);
+        const bf16x2 lo = {(__bf16)(p0 - __uint_as_float(hbits << 16)),
+                           (__bf16)(p1 - __uint_as_float(hbits & 0xFFFF0000u))};
+        hpk[q >> 2][q & 3] = hbits;
+        lpk[q >> 2][q & 3] = __builtin_bit_cast(uint32_t, lo);
       }
+      const bf16x8 phi[2] = {__builtin_bit_cast(bf16x8, hpk[0]), __builtin_bit_cast(bf16x8, hpk[1])};
+      const bf16x8 plo[2] = {__builtin_bit_cast(bf16x8, lpk[0]), __builtin_bit_cast(bf16x8, lpk[1])};
       l_run += psum;
 
       // O^T[128 x 32 rows] += V^T . P over two 16-token k steps
