@@ -20,6 +20,16 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
+def assert_device_flags(ws, wl) -> None:
+    """No error bit in the workspace's device flag word. Bit 3 (a worker raised a row's
+    reference maximum and rescaled it) is expected only where the workload plants high-score
+    keys: a planted key met past a worker's first tile raises the reference."""
+    import sequence_sharded_kv_amd as dcp
+    flags = dcp.dcp_read_device_flags(ws)
+    allowed = (0, 8) if getattr(wl, "plants_per_head", 0) else (0,)
+    assert flags in allowed, flags
+
+
 def host_view(t):
     """numpy copy of a device tensor: bf16 as uint16 bit patterns, others as-is."""
     if t.dtype == torch.bfloat16:

@@ -64,9 +64,11 @@ def test_kernel_family_follows_the_row_count(bench):
     assert bench.kernel_family(workload("mla-64h-b512"), 2) == "mla-pair"   # 128 rows, 8 waves
     assert bench.kernel_family(workload("mla-128h"), 1) == "mla-pair"
     assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=16), 5) == "mla-pair"
-    assert bench.kernel_family(workload("gqa-g16"), 1) == "gqa-mfma"
+    assert bench.kernel_family(workload("gqa-g16"), 1) == "gqa-chunk"   # 16 of 32 rows
     assert bench.kernel_family(workload("gqa-g16"), 2) == "gqa-chunk"
-    assert bench.kernel_family(workload("gqa-long"), 2) == "gqa-mfma"   # 8 x 2 = 16 rows
+    assert bench.kernel_family(workload("gqa-long"), 1) == "gqa-chunk"  # 8 of 32 rows
+    assert bench.kernel_family(workload("gqa-g16").replace(num_q_heads=16, head_dim_qk=64,
+                                                           head_dim_v=64), 1) == "gqa-mfma"
     assert bench.kernel_family(workload("gqa-tiny"), 1) == "gqa-valu"   # fp32
 
 

@@ -11,8 +11,8 @@ import pytest
 import torch
 
 import sequence_sharded_kv_amd as dcp
-from gpu_helpers import (assert_close, host_inputs_of, oracle_partials, run_fused, run_partial,
-                         say)
+from gpu_helpers import (assert_close, assert_device_flags, host_inputs_of, oracle_partials,
+                         run_fused, run_partial, say)
 from oracle import oracle as O
 from workloads import make_device_inputs, workload
 
@@ -30,7 +30,7 @@ def _run(name):
     out, out_lse, ws = run_fused(wl, inp, bounds)
     po, pl, _ = run_partial(wl, inp, bounds, ws=ws)
     torch.cuda.synchronize()
-    assert dcp.dcp_read_device_flags(ws) == 0
+    assert_device_flags(ws, wl)
     # properties over every output: finite, and O is a convex combination of value rows
     assert torch.isfinite(out).all() and torch.isfinite(out_lse).all()
     vals = inp["kv_cache"][..., : wl.head_dim_v] if wl.kind == "mla" else inp["v_cache"]

@@ -9,7 +9,8 @@ import pytest
 import torch
 
 import sequence_sharded_kv_amd as dcp
-from gpu_helpers import assert_close, host_inputs_of, run_partial, say, shape_of, to_device
+from gpu_helpers import (assert_close, assert_device_flags, host_inputs_of, run_partial, say,
+                         shape_of, to_device)
 from oracle import oracle as O
 from workloads import make_host_inputs, make_queries, workload
 
@@ -91,7 +92,7 @@ def test_multi_token_partials_and_fused_match_oracle(name, wl_name, lengths, T, 
     dcp.dcp_merge_lse(po.view(B, S, T * Hq, Dv), pl.view(B, S, T * Hq), mo.view(B, T * Hq, Dv),
                       ml.view(B, T * Hq))
     torch.cuda.synchronize()
-    assert dcp.dcp_read_device_flags(ws) == 0
+    assert_device_flags(ws, wl)
     _, caches, bt, _ = host_inputs_of(wl, inp)
     ro, rl = O.partial_attention_multi(wl.kind, wl.dtype, qh, caches, bt,
                                        np.asarray(bounds_np, np.int64), wl.block_size,
@@ -148,7 +149,7 @@ def test_prefill_chunk_sampled_tokens_match_oracle(name, wl_name, lengths, T, ov
     out_lse = torch.empty((B, T, Hq), dtype=torch.float32, device="cuda")
     dcp.dcp_decode_attn_multi(sh, T, q, k, v, inp["block_table"], bounds, ws, out, out_lse)
     torch.cuda.synchronize()
-    assert dcp.dcp_read_device_flags(ws) == 0
+    assert_device_flags(ws, wl)
     assert torch.isfinite(out).all() and torch.isfinite(po).all()
     rng = np.random.default_rng(5)
     pick = sorted({0, 1, T // 2, T - 2, T - 1} |

@@ -6,8 +6,8 @@ import pytest
 import torch
 
 import sequence_sharded_kv_amd as dcp
-from gpu_helpers import (assert_close, host_inputs_of, oracle_full, oracle_partials, run_fused,
-                         run_partial, say, shape_of, to_device)
+from gpu_helpers import (assert_close, assert_device_flags, host_inputs_of, oracle_full,
+                         oracle_partials, run_fused, run_partial, say, shape_of, to_device)
 from oracle import oracle as O
 from workloads import make_host_inputs, workload
 
@@ -75,7 +75,7 @@ def test_partials_merge_and_fused_match_oracle(name, wl_name, lengths, over):
     dcp.dcp_merge_lse(po, pl, out, out_lse)
     fo, fl, _ = run_fused(wl, inp, bounds, ws=ws)
     torch.cuda.synchronize()
-    assert dcp.dcp_read_device_flags(ws) == 0
+    assert_device_flags(ws, wl)
     ro, rl = oracle_partials(wl, hin, bounds_np)
     assert_close(po.cpu().numpy(), pl.cpu().numpy(), ro, rl, wl.dtype, f"{name} partials")
     fo_ref, fl_ref = oracle_full(wl, hin)
@@ -168,10 +168,12 @@ def test_any_partition_merges_to_full_attention(wl_name, over, lengths):
     ("mla-64h-b512", dict(batch=2, block_size=16), [500, 77]),         # tiles over 2 pages
     ("mla-64h-b512", dict(batch=2, num_q_heads=32, block_size=16), [300, 50]),
     ("mla-128h", dict(batch=2, block_size=16), [400, 39]),
-    ("gqa-g16", dict(batch=3), [1000, 77, 3001]),                       # MFMA kernel
+    ("gqa-g16", dict(batch=3), [1000, 77, 3001]),                       # 32-row kernel
+    ("gqa-g16", dict(batch=2, num_q_heads=16, head_dim_qk=64, head_dim_v=64),
+     [700, 45]),                                                        # 16-row kernel
     ("gqa-g16", dict(batch=2, dtype="f32"), [700, 45]),                 # VALU kernel
 ], ids=["mla-64h", "mla-32h", "mla-128h", "mla-64h-bs16", "mla-32h-bs16", "mla-128h-bs16",
-        "gqa-g16", "gqa-g16-f32"])
+        "gqa-g16", "gqa-g4-d64", "gqa-g16-f32"])
 def test_unused_slots_past_the_context_stay_out_of_the_output(wl_name, over, lengths):
     """A page's slots past the context end may hold anything in a real cache. Filled with NaN
     here, they must not reach the output: masked tokens get weight 0, and 0 * NaN would
@@ -202,7 +204,7 @@ def test_unused_slots_past_the_context_stay_out_of_the_output(wl_name, over, len
     bounds = torch.from_numpy(bounds_np).cuda()
     fo, fl, ws = run_fused(wl, inp, bounds)
     torch.cuda.synchronize()
-    assert dcp.dcp_read_device_flags(ws) == 0
+    assert_device_flags(ws, wl)
     o, l = fo.cpu().numpy(), fl.cpu().numpy()
     assert np.isfinite(o).all() and np.isfinite(l).all()
     fo_ref, fl_ref = oracle_full(wl, hin)

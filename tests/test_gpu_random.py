@@ -8,7 +8,8 @@ import pytest
 import torch
 
 import sequence_sharded_kv_amd as dcp
-from gpu_helpers import assert_close, host_inputs_of, say, shape_of, to_device
+from gpu_helpers import (assert_close, assert_device_flags, host_inputs_of, say, shape_of,
+                         to_device)
 from oracle import oracle as O
 from workloads import make_host_inputs, make_queries, workload
 
@@ -70,7 +71,7 @@ def test_random_shape_matches_oracle(name, base, over, T):
     dcp.dcp_decode_attn_multi(sh, T, q, k, v, inp["block_table"],
                               torch.from_numpy(bounds_np).cuda(), ws, out, lse)
     torch.cuda.synchronize()
-    assert dcp.dcp_read_device_flags(ws) == 0
+    assert_device_flags(ws, wl)
     _, caches, bt, _ = host_inputs_of(wl, inp)
     ro, rl = O.partial_attention_multi(wl.kind, wl.dtype, qh, caches, bt,
                                        np.asarray(bounds_np, np.int64), wl.block_size,
