@@ -1,19 +1,20 @@
-// GQA partial attention for units of 32 to 128 query rows per KV head (several query tokens
-// per request, or a prefill chunk), bf16, head_dim 128.
+// GQA partial attention, bf16, head_dim 128: units of 32 to 128 query rows of one KV head
+// (one decode token's G heads padded to 32, several query tokens per request, or a prefill
+// chunk in groups of 128).
 //
-// The 16-row GQA kernel streams a shard's K/V once per 16 rows. Here a workgroup of NW waves
-// owns 32 * NW rows of one KV head and the waves share each K/V tile through a three-slot LDS
-// ring filled two tiles ahead, so the shard's pages are read once per 32 * NW rows. Per
-// 32-token tile, wave w (rows 32 w .. 32 w + 31):
+// A workgroup of NW waves owns 32 * NW rows of one KV head and the waves share each K/V tile
+// through a three-slot LDS ring filled two tiles ahead, so the shard's pages are read once per
+// 32 * NW rows. Per 32-token tile, wave w (rows 32 w .. 32 w + 31):
 //   S[32 tok x 32 rows] = K[32 x 128] . Q^T[128 x 32]   8 x v_mfma_f32_32x32x16_bf16, K rows
 //                                                       from LDS, the rows' Q in registers;
-//   online softmax per row (a lane holds 16 scores of its row, the other 16 are in lane
-//   l ^ 32), each row masked at its own causal limit;
+//   weights per row against a reference max (a lane holds 16 scores of its row, the other 16
+//   are in lane l ^ 32), each row masked at its own causal limit where the tile is not fully
+//   visible;
 //   O^T[128 x 32] += V^T[128 x 32 tok] . P[32 tok x 32 rows]   4 M blocks x 2 k steps, V read
 //                                                       transposed from LDS, P as a bf16 high
 //                                                       part and remainder (two MFMAs).
-// The accumulator is 64 registers, so the running max is moved (and O rescaled) whenever it
-// grows, and two waves share each SIMD.
+// The tile loop is unrolled over the ring's slots so that every LDS read is a fixed per-lane
+// offset plus an immediate. Two waves share each SIMD.
 //
 // Tile layout: per slot a K tile then a V tile, each 32 rows x 256 B; 16-byte chunk c of row r
 // sits at position c ^ sw(r), sw(r) = ((r & 3) << 2) | ((r >> 2) & 3). A 256-byte row spans all

@@ -1,4 +1,5 @@
-// GQA partial attention with bf16 MFMA, for groups of up to 16 query heads per KV head.
+// GQA partial attention with bf16 MFMA, for groups of up to 16 query heads per KV head (the
+// dispatcher uses it for head dim 64; head dim 128 goes to the 32-row kernel in k_gqa_chunk.hip).
 //
 // One wave is one stream-K worker and owns (segment of a (request, shard, kv head) unit) at
 // a time. Per 32-token tile:
