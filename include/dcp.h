@@ -224,7 +224,7 @@ dcp_status dcp_decode_attn_noalloc(const dcp_attn_shape* shape, const void* q,
  *   the workspace must hold dcp_workspace_bytes_multi(shape, q_len) bytes. dcp_merge_lse merges
  *   these partials when called with num_heads = q_len * Hq.
  * The KV pages are streamed once per group of query rows that share them: MLA takes up to 128
- * rows (q_len * Hq) in one pass, GQA up to 128 rows (q_len * Hq / Hkv) per KV head for bf16
+ * rows (q_len * Hq) in one pass, GQA up to 256 rows (q_len * Hq / Hkv) per KV head for bf16
  * head dim 128 and 16 for the other GQA shapes; a prefill
  * chunk therefore streams each shard's pages once per row group, as a flash-attention query
  * block does. The fused call keeps B * S * q_len * Hq partials in the workspace. Errors

@@ -119,11 +119,11 @@ dcp_status make_plan(const dcp_attn_shape* sh, int32_t Tq, dcp::Plan* plan) {
   if (sh->kv_kind == DCP_KV_GQA) {
     const int32_t D = sh->head_dim_qk;
     if (sh->dtype == DCP_BF16 && G <= 16 && D == 128) {
-      // units of 32 to 128 rows share each K/V tile (fewer rows are padded to 32: the
+      // units of 32 to 256 rows share each K/V tile (fewer rows are padded to 32: the
       // 32-row kernel streams a head's pages faster than the 16-row one even half empty)
       k = Kernel::kGqaChunk;
       ru = 32;
-      while (ru < rows && ru < 128) ru *= 2;
+      while (ru < rows && ru < 256) ru *= 2;
       pmax = kMaxWorkersChunk;
     } else {
       if (sh->dtype == DCP_BF16 && G <= 16 && (D == 64 || D == 128))

@@ -1,6 +1,6 @@
-// GQA partial attention, bf16, head_dim 128: units of 32 to 128 query rows of one KV head
+// GQA partial attention, bf16, head_dim 128: units of 32 to 256 query rows of one KV head
 // (one decode token's G heads padded to 32, several query tokens per request, or a prefill
-// chunk in groups of 128).
+// chunk in groups of 256).
 //
 // A workgroup of NW waves owns 32 * NW rows of one KV head and the waves share each K/V tile
 // through a three-slot LDS ring filled two tiles ahead, so the shard's pages are read once per
@@ -373,7 +373,8 @@ int32_t gqa_chunk_workers(int device, int32_t Ru, int32_t max_workers) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
       cus <= 0)
     cus = 256;
-  // two waves per SIMD (8 per CU) by registers; 48 KB of LDS per workgroup
+  // two waves per SIMD (8 per CU) by registers, so one 8-wave workgroup (256 rows) per CU;
+  // 48 KB of LDS per workgroup
   const int nw = Ru / 32;
   const int by_regs = 8 / nw, by_lds = 160 / 48;
   const int per_cu = by_regs < by_lds ? by_regs : by_lds;
@@ -386,6 +387,7 @@ hipError_t launch_gqa_chunk(const AttnArgs& a, hipStream_t stream) {
     case 1: hipLaunchKernelGGL((gqa_chunk_kernel<1>), dim3(a.P), dim3(64), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((gqa_chunk_kernel<2>), dim3(a.P), dim3(128), 0, stream, a); break;
     case 4: hipLaunchKernelGGL((gqa_chunk_kernel<4>), dim3(a.P), dim3(256), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((gqa_chunk_kernel<8>), dim3(a.P), dim3(512), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -53,6 +53,8 @@ CASES = [
     ("gqa-d256-valu-t3", "gqa-g16", [700, 70], 3, dict(batch=2, head_dim_qk=256,
                                                       head_dim_v=256)),
     ("gqa-g16-t5-bs24", "gqa-g16", [500, 49], 5, dict(batch=2, block_size=24)),
+    # 160 rows per KV head: one 8-wave unit of 256 rows, 96 of them padding
+    ("gqa-g16-t10-256rows", "gqa-g16", [700, 33], 10, dict(batch=2)),
     # prefill chunks: many row groups per shard, chunks that cross shard boundaries, and a
     # request shorter than its chunk
     ("mla-64h-chunk64", "mla-64h-b512", [1500, 300], 64, dict(batch=2, num_shards=4)),
