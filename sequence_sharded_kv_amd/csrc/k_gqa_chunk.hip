@@ -4,7 +4,9 @@
 //
 // A workgroup of NW waves owns 32 * NW rows of one KV head and the waves share each K/V tile
 // through a three-slot LDS ring filled two tiles ahead, so the shard's pages are read once per
-// 32 * NW rows. Per 32-token tile, wave w (rows 32 w .. 32 w + 31):
+// 32 * NW rows. Tiles hold 32 tokens, or 64 in the 8-wave instance (one workgroup per CU, so
+// its 96 KB of LDS fit, and the per-tile work of the copies, the maximum and the waits is
+// spread over twice the scores). Per 32 tokens of a tile, wave w (rows 32 w .. 32 w + 31):
 //   S[32 tok x 32 rows] = K[32 x 128] . Q^T[128 x 32]   8 x v_mfma_f32_32x32x16_bf16, K rows
 //                                                       from LDS, the rows' Q in registers;
 //   weights per row against a reference max (a lane holds 16 scores of its row, the other 16
@@ -47,12 +49,17 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* lo, const char* hi) {
 }
 }  // namespace gchunk
 
-template <int NW>  // waves per workgroup, 32 rows each
+template <int NW, int kT>  // waves per workgroup (32 rows each); tokens per tile (32 or 64)
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gqa_chunk_kernel(AttnArgs a) {
   using namespace gchunk;
-  constexpr int kDma = 16 / NW;  // copies per wave per tile (8 K + 8 V instructions)
-  __shared__ __attribute__((aligned(1024))) char lds[kSlots * kSlotB];
+  static_assert(kT == 32 || kT == 64, "tile of 32 or 64 tokens");
+  constexpr int kH = kT / 32;               // 32-token halves of a tile
+  constexpr int kTB = kT * kRowB;           // one K or V tile
+  constexpr int kSB = 2 * kTB;              // K tile then V tile
+  constexpr int kCp = kT / 4 / NW;          // copy instructions per wave per K (or V) tile
+  constexpr int kDma = 2 * kCp;             // copies per wave per tile
+  __shared__ __attribute__((aligned(1024))) char lds[kSlots * kSB];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5;      // lane half: k slice of the 32x32x16 operand layouts
@@ -72,8 +79,9 @@ gqa_chunk_kernel(AttnArgs a) {
   const int bs_shift = __builtin_ctz((unsigned)a.bs);
   const uint32_t lds0 = lds_u32(&lds[0]);
 
-  // Per-lane LDS byte offsets within a slot, fixed for the kernel; a slot's base and the
-  // value product's second 16-token k step (16 rows = 4096 B further) are immediates.
+  // Per-lane LDS byte offsets within a slot, fixed for the kernel; a slot's base, a tile's
+  // second 32-token half (8192 B further) and the value product's second 16-token k step
+  // (4096 B) are immediates.
   //   score reads: row c32, chunk (2 ks + g) ^ sw(c32);
   //   transposed value reads: 16-lane group q4, lane L reads rows 4 (q4 >> 1) + (L >> 2) (+ 8),
   //   chunk 4 mt + 2 (q4 & 1) + ((L & 3) >> 1), byte 8 (L & 1) of the chunk. sw(r) depends on
@@ -92,7 +100,7 @@ gqa_chunk_kernel(AttnArgs a) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int r = vr + 8 * hf;
-        voff[2 * mt + hf] = kTileB + r * kRowB + vw + 16 * ((vc + 4 * mt) ^ sw(r));
+        voff[2 * mt + hf] = kTB + r * kRowB + vw + 16 * ((vc + 4 * mt) ^ sw(r));
       }
 #pragma unroll
     for (int q = 0; q < 8; ++q) asm volatile("" : "+v"(koff[q]), "+v"(voff[q]));
@@ -115,7 +123,7 @@ gqa_chunk_kernel(AttnArgs a) {
     const bool first = (gg == g0);
     const int32_t* brow = a.block_table + (int64_t)b * a.max_blocks;
     const int32_t t0i = (int32_t)t0, t1i = (int32_t)t1;
-    const int32_t ntiles = (t1i - t0i + 31) / 32;  // >= 1
+    const int32_t ntiles = (t1i - t0i + kT - 1) / kT;  // >= 1
     auto page_idx = [&](int32_t t) -> int32_t { return bs_pow2 ? (t >> bs_shift) : t / a.bs; };
     const int32_t plast_seg = page_idx(t1i - 1);
 
@@ -137,14 +145,15 @@ gqa_chunk_kernel(AttnArgs a) {
     };
 
     // Queue tile i into slot i % kSlots: this wave's copy instructions k = wv + NW m of the K
-    // tile and of the V tile. Lane t (and t + 32) finds token tile + t's row in the caches (-1
-    // for an invalid page) with one lane permute of the page ids; each copy lane then fetches
-    // the row index of its own row the same way. Returns the tile's valid-token mask.
-    auto issue_tile = [&](int32_t i) -> uint32_t {
-      const int32_t tile = t0i + 32 * i;
-      const int32_t tl = (tile + 31 < t1i ? tile + 31 : t1i - 1);
+    // tile and of the V tile (one instruction fills rows 4k .. 4k + 3). Lane t < kT (t and
+    // t + 32 for 32-token tiles) finds token tile + t's row in the caches (all ones for an
+    // invalid page) with one lane permute of the page ids; each copy lane then fetches the
+    // row index of its own row the same way. Returns the tile's valid-token mask.
+    auto issue_tile = [&](int32_t i) -> uint64_t {
+      const int32_t tile = t0i + kT * i;
+      const int32_t tl = (tile + kT - 1 < t1i ? tile + kT - 1 : t1i - 1);
       ensure_pages(page_idx(tile), page_idx(tl));
-      const int32_t t = tile + c32;
+      const int32_t t = tile + (kT == 64 ? lane : c32);
       const int32_t tc = t < t1i ? t : t1i - 1;
       const int32_t blk = __builtin_amdgcn_ds_bpermute(4 * (page_idx(tc) - pchunk), pid);
       const bool page_ok = blk >= 0 && blk < a.num_blocks;
@@ -155,11 +164,11 @@ gqa_chunk_kernel(AttnArgs a) {
           page_ok ? ((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)kvh) * (uint32_t)a.bs + slot
                   : 0xFFFFFFFFu;
       bad |= __any(!page_ok) ? 1 : 0;
-      const uint32_t mask = (uint32_t)__ballot(lane < 32 && page_ok && t < t1i);
-      const uint32_t base = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((i % kSlots) * kSlotB));
+      const uint64_t mask = (uint64_t)__ballot((kT == 64 || lane < 32) && page_ok && t < t1i);
+      const uint32_t base = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((i % kSlots) * kSB));
       const int sub = lane >> 4, p = lane & 15;
 #pragma unroll
-      for (int m = 0; m < 8 / NW; ++m) {
+      for (int m = 0; m < kCp; ++m) {
         const int k = wv + NW * m;  // rows 4k .. 4k + 3
         const int r = 4 * k + sub;
         const uint32_t rr = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * r, (int)row);
@@ -168,7 +177,7 @@ gqa_chunk_kernel(AttnArgs a) {
         const char* ks = ok ? Kc + (uint64_t)rr * kRowB + chunk : a.zero_row + chunk;
         const char* vs = ok ? Vc + (uint64_t)rr * kRowB + chunk : a.zero_row + chunk;
         dma16(ks, base + k * 1024);
-        dma16(vs, base + kTileB + k * 1024);
+        dma16(vs, base + kTB + k * 1024);
       }
       return mask;
     };
@@ -206,67 +215,76 @@ gqa_chunk_kernel(AttnArgs a) {
     float m_ref = kNegInf, l_run = 0.f;
     const float sl2 = a.scale_log2;
 
-    uint32_t maskv = 0;  // lane s: valid-token mask of the tile in slot s
+    uint32_t mlo = 0, mhi = 0;  // lane s: valid-token mask of the tile in slot s (low, high)
     int32_t issued = 0;
+    auto issue_next = [&]() {
+      const uint64_t m = issue_tile(issued);
+      const bool mine = lane == issued % kSlots;
+      mlo = mine ? (uint32_t)m : mlo;
+      mhi = mine ? (uint32_t)(m >> 32) : mhi;
+      ++issued;
+    };
     for (int k = 0; k < kSlots - 1; ++k)
-      if (issued < ntiles) {
-        const uint32_t m = issue_tile(issued);
-        maskv = (lane == issued % kSlots) ? m : maskv;
-        ++issued;
-      }
+      if (issued < ntiles) issue_next();
     wait_tiles(issued - 1);
     __syncthreads();
 
     // one tile in slot S (a compile-time constant: the LDS offsets are immediates)
     auto body = [&](auto slot_tag, int32_t i) {
       constexpr int S = decltype(slot_tag)::value;
-      if (issued < ntiles) {
-        const uint32_t m = issue_tile(issued);
-        maskv = (lane == issued % kSlots) ? m : maskv;
-        ++issued;
-      }
-      const int32_t tile = t0i + 32 * i;
+      if (issued < ntiles) issue_next();
+      const int32_t tile = t0i + kT * i;
       const int32_t dl = lim - tile;
-      const uint32_t mask = __builtin_amdgcn_readlane(maskv, S) &
-                            (dl < 0 ? 0u : dl >= 31 ? 0xFFFFFFFFu : (2u << dl) - 1u);
-      const bool full = __ballot(mask != 0xFFFFFFFFu) == 0;  // wave-uniform
-      const char* tb = lds + S * kSlotB;
+      const uint64_t tmask = ((uint64_t)__builtin_amdgcn_readlane(mhi, S) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane(mlo, S);
+      const uint64_t cmask = dl < 0 ? 0ull : dl >= kT - 1 ? ~0ull : (2ull << dl) - 1ull;
+      const uint64_t all = kT == 64 ? ~0ull : 0xFFFFFFFFull;
+      const uint64_t mask = tmask & cmask & all;
+      const bool full = __ballot(mask != all) == 0;  // wave-uniform
+      const char* tb = lds + S * kSB;
 
-      // S[32 tok x 32 rows] = K . Q^T
-      f32x16 st;
+      // S[kT tok x 32 rows] = K . Q^T, one 32-token half at a time
+      f32x16 st[kH];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = 0.f;
-      bf16x8 kbuf[4];
+      for (int h = 0; h < kH; ++h) {
+        bf16x8 kbuf[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kbuf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(tb + koff[ks]));
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 kop = kbuf[ks & 3];
-        if (ks + 4 < 8)
-          kbuf[ks & 3] = __builtin_bit_cast(bf16x8, *(const u32x4*)(tb + koff[ks + 4]));
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], st, 0, 0, 0);
+        for (int ks = 0; ks < 4; ++ks)
+          kbuf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(tb + 8192 * h + koff[ks]));
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8 kop = kbuf[ks & 3];
+          if (ks + 4 < 8)
+            kbuf[ks & 3] =
+                __builtin_bit_cast(bf16x8, *(const u32x4*)(tb + 8192 * h + koff[ks + 4]));
+          st[h] = ks == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[0], f32x16{}, 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], st[h], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
 
-      // row c32's maximum over the tile; st[r] is token 8 (r / 4) + 4 g + r % 4. A tile with
-      // every token visible skips the masks (their bits are formed inside the masked branch
-      // only).
-      uint32_t hmask = 0;
-      auto valid = [&](int r) { return ((hmask >> (8 * (r >> 2) + (r & 3))) & 1u) != 0u; };
+      // row c32's maximum over the tile; st[h][r] is token 32 h + 8 (r / 4) + 4 g + r % 4. A
+      // tile with every token visible skips the masks (their bits are formed inside the
+      // masked branch only).
       float tmax = kNegInf;
       if (full) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[r]);
+        for (int h = 0; h < kH; ++h)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[h][r]);
       } else {
-        hmask = mask >> (4 * g);
+        uint64_t hmask = mask >> (4 * g);
         asm volatile("" : "+v"(hmask));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          // a masked score becomes -inf here, so the weights below need no second mask
-          st[r] = valid(r) ? st[r] : kNegInf;
-          tmax = fmaxf(tmax, st[r]);
-        }
+        for (int h = 0; h < kH; ++h)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            // a masked score becomes -inf here, so the weights below need no second mask
+            const bool v = ((hmask >> (32 * h + 8 * (r >> 2) + (r & 3))) & 1ull) != 0ull;
+            st[h][r] = v ? st[h][r] : kNegInf;
+            tmax = fmaxf(tmax, st[h][r]);
+          }
       }
       {
         auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
@@ -291,36 +309,44 @@ gqa_chunk_kernel(AttnArgs a) {
       // token yet (m_ref = -inf), where every score of the tile is masked and the weights are
       // set to zero instead.
       const float nm = m_ref == kNegInf ? 0.f : -m_ref;
-      float pv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(__builtin_fmaf(st[r], sl2, nm));
-      // bf16 high parts packed in pairs; the remainders from the unpacked highs
+      // bf16 high parts packed in pairs; the remainders from the unpacked highs; k step kk of
+      // half h is operand 2 h + kk
       float psum = 0.f;
-      u32x4 hpk[2], lpk[2];
+      bf16x8 phi[2 * kH], plo[2 * kH];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float p0 = pv[2 * q], p1 = pv[2 * q + 1];
-        psum += p0 + p1;
-        typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-        const bf16x2 h = {(__bf16)p0, (__bf16)p1};
-        const uint32_t hbits = __builtin_bit_cast(uint32_t, h);
-        const bf16x2 lo = {(__bf16)(p0 - __uint_as_float(hbits << 16)),
-                           (__bf16)(p1 - __uint_as_float(hbits & 0xFFFF0000u))};
-        hpk[q >> 2][q & 3] = hbits;
-        lpk[q >> 2][q & 3] = __builtin_bit_cast(uint32_t, lo);
+      for (int h = 0; h < kH; ++h) {
+        u32x4 hpk[2], lpk[2];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float p0 = fast_exp2(__builtin_fmaf(st[h][2 * q], sl2, nm));
+          const float p1 = fast_exp2(__builtin_fmaf(st[h][2 * q + 1], sl2, nm));
+          psum += p0 + p1;
+          typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+          const bf16x2 hh = {(__bf16)p0, (__bf16)p1};
+          const uint32_t hbits = __builtin_bit_cast(uint32_t, hh);
+          const bf16x2 lo = {(__bf16)(p0 - __uint_as_float(hbits << 16)),
+                             (__bf16)(p1 - __uint_as_float(hbits & 0xFFFF0000u))};
+          hpk[q >> 2][q & 3] = hbits;
+          lpk[q >> 2][q & 3] = __builtin_bit_cast(uint32_t, lo);
+        }
+        phi[2 * h] = __builtin_bit_cast(bf16x8, hpk[0]);
+        phi[2 * h + 1] = __builtin_bit_cast(bf16x8, hpk[1]);
+        plo[2 * h] = __builtin_bit_cast(bf16x8, lpk[0]);
+        plo[2 * h + 1] = __builtin_bit_cast(bf16x8, lpk[1]);
       }
-      const bf16x8 phi[2] = {__builtin_bit_cast(bf16x8, hpk[0]), __builtin_bit_cast(bf16x8, hpk[1])};
-      const bf16x8 plo[2] = {__builtin_bit_cast(bf16x8, lpk[0]), __builtin_bit_cast(bf16x8, lpk[1])};
       l_run += psum;
 
-      // O^T[128 x 32 rows] += V^T . P over two 16-token k steps
+      // O^T[128 x 32 rows] += V^T . P over the tile's 16-token k steps
 #pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) {
-        const int kk = s2 >> 2, mt = s2 & 3;
-        const bf16x8 vop = tr_pair(tb + 4096 * kk + voff[2 * mt], tb + 4096 * kk + voff[2 * mt + 1]);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, phi[kk], acc[mt], 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, plo[kk], acc[mt], 0, 0, 0);
-      }
+      for (int h = 0; h < kH; ++h)
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) {
+          const int kk = s2 >> 2, mt = s2 & 3;
+          const char* vb = tb + 8192 * h + 4096 * kk;
+          const bf16x8 vop = tr_pair(vb + voff[2 * mt], vb + voff[2 * mt + 1]);
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, phi[2 * h + kk], acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, plo[2 * h + kk], acc[mt], 0, 0, 0);
+        }
       // tile i + 1 has landed and every wave is past tile i (its slot is refilled next)
       wait_tiles(issued - (i + 2));
       __syncthreads();
@@ -374,7 +400,7 @@ int32_t gqa_chunk_workers(int device, int32_t Ru, int32_t max_workers) {
       cus <= 0)
     cus = 256;
   // two waves per SIMD (8 per CU) by registers, so one 8-wave workgroup (256 rows) per CU;
-  // 48 KB of LDS per workgroup
+  // 48 KB of LDS per workgroup (96 KB for the 8-wave instance's 64-token tiles)
   const int nw = Ru / 32;
   const int by_regs = 8 / nw, by_lds = 160 / 48;
   const int per_cu = by_regs < by_lds ? by_regs : by_lds;
@@ -384,10 +410,10 @@ int32_t gqa_chunk_workers(int device, int32_t Ru, int32_t max_workers) {
 
 hipError_t launch_gqa_chunk(const AttnArgs& a, hipStream_t stream) {
   switch (a.Ru / 32) {
-    case 1: hipLaunchKernelGGL((gqa_chunk_kernel<1>), dim3(a.P), dim3(64), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((gqa_chunk_kernel<2>), dim3(a.P), dim3(128), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((gqa_chunk_kernel<4>), dim3(a.P), dim3(256), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((gqa_chunk_kernel<8>), dim3(a.P), dim3(512), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((gqa_chunk_kernel<1, 32>), dim3(a.P), dim3(64), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((gqa_chunk_kernel<2, 32>), dim3(a.P), dim3(128), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((gqa_chunk_kernel<4, 32>), dim3(a.P), dim3(256), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((gqa_chunk_kernel<8, 64>), dim3(a.P), dim3(512), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
