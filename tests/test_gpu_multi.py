@@ -53,7 +53,9 @@ CASES = [
     ("gqa-d256-valu-t3", "gqa-g16", [700, 70], 3, dict(batch=2, head_dim_qk=256,
                                                       head_dim_v=256)),
     ("gqa-g16-t5-bs24", "gqa-g16", [500, 49], 5, dict(batch=2, block_size=24)),
-    # 160 rows per KV head: one 8-wave unit of 256 rows, 96 of them padding
+    # 48 rows per KV head: one 2-wave unit of 64 rows; 160 rows: one 8-wave unit of 256 rows
+    # on 64-token tiles, 96 of them padding
+    ("gqa-g16-t3-64rows", "gqa-g16", [900, 70], 3, dict(batch=2)),
     ("gqa-g16-t10-256rows", "gqa-g16", [700, 33], 10, dict(batch=2)),
     # prefill chunks: many row groups per shard, chunks that cross shard boundaries, and a
     # request shorter than its chunk
