@@ -57,6 +57,10 @@ CASES = [
     # on 64-token tiles, 96 of them padding
     ("gqa-g16-t3-64rows", "gqa-g16", [900, 70], 3, dict(batch=2)),
     ("gqa-g16-t10-256rows", "gqa-g16", [700, 33], 10, dict(batch=2)),
+    # 64-token tiles across pages: 24-token pages (non-power-of-two) and one-token pages (a
+    # tile spans 64 pages, the most one lookup of page ids holds)
+    ("gqa-g16-t10-bs24", "gqa-g16", [600, 45], 10, dict(batch=2, block_size=24)),
+    ("gqa-g16-t12-bs1", "gqa-g16", [300, 20], 12, dict(batch=2, block_size=1)),
     # prefill chunks: many row groups per shard, chunks that cross shard boundaries, and a
     # request shorter than its chunk
     ("mla-64h-chunk64", "mla-64h-b512", [1500, 300], 64, dict(batch=2, num_shards=4)),
