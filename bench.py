@@ -89,6 +89,8 @@ def kernel_family(wl, q_len=1):
         # units of 64 query rows take the 12-wave ring kernel, of 128 the 8-wave fp16 pair
         # kernel, smaller units the 16-rows-per-wave kernel
         rows = q_len * wl.num_q_heads
+        if 128 < rows <= 192:
+            return "mla-ring"   # three 64-row units rather than two of 128
         return "mla-pair" if rows > 64 else "mla-ring" if rows > 32 else "mla"
     g = wl.num_q_heads // wl.num_kv_heads
     if wl.dtype == "bf16" and g <= 16 and wl.head_dim_qk == 128:

@@ -141,6 +141,9 @@ dcp_status make_plan(const dcp_attn_shape* sh, int32_t Tq, dcp::Plan* plan) {
     // waves of 16 rows, a power of two of them up to 8 per workgroup
     ru = 16;
     while (ru < rows && ru < 128) ru *= 2;
+    // 129 to 192 rows: three 64-row units stream the KV faster than two of 128 rows whose
+    // second is at least half padding
+    if (rows > 128 && rows <= 192) ru = 64;
     // units of 64 or 128 rows run one workgroup per CU (256 on gfx950), smaller ones two
     pmax = ru >= 64 ? kMaxWorkersMla / 2 : kMaxWorkersMla;
   }
