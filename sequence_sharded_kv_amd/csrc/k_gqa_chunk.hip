@@ -18,7 +18,7 @@
 // The tile loop is unrolled over the ring's slots so that every LDS read is a fixed per-lane
 // offset plus an immediate. Two waves share each SIMD.
 //
-// Tile layout: per slot a K tile then a V tile, each 32 rows x 256 B; 16-byte chunk c of row r
+// Tile layout: per slot a K tile then a V tile, each kT rows x 256 B; 16-byte chunk c of row r
 // sits at position c ^ sw(r), sw(r) = ((r & 3) << 2) | ((r >> 2) & 3). A 256-byte row spans all
 // 64 banks once, so a chunk's banks depend on its position only; the swizzle spreads the K
 // reads (32 rows, one chunk each) and the transposed V reads over distinct banks. One copy
@@ -33,8 +33,6 @@ namespace dcp {
 namespace gchunk {
 constexpr int kD = 128;
 constexpr int kRowB = kD * 2;           // 256 bytes per token row
-constexpr int kTileB = 32 * kRowB;      // 8 KB: one K or V tile
-constexpr int kSlotB = 2 * kTileB;      // K tile then V tile
 constexpr int kSlots = 3;
 __device__ __forceinline__ int sw(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 typedef __attribute__((ext_vector_type(16))) float f32x16;
