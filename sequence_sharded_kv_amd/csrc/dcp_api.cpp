@@ -191,11 +191,23 @@ dcp_status device_fail(hipError_t e, const char* what) {
   return fail(DCP_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Shared front half of the two attention entry points.
+// Fused MLA calls of 129 to 192 query rows run in two passes over the KV: the first 128 rows
+// (128 / Hq tokens) as one 128-row unit, the remaining tokens as one unit of at most 64 rows.
+// Returns the first pass's token count, or 0 where the call runs in one pass.
+int32_t split_tokens(const dcp_attn_shape* sh, int32_t Tq) {
+  if (sh->kv_kind != DCP_KV_MLA) return 0;
+  const int64_t Hq = sh->num_q_heads, rows = Hq * Tq;
+  return (rows > 128 && rows <= 192 && Hq <= 64 && 128 % Hq == 0) ? (int32_t)(128 / Hq) : 0;
+}
+
+// Shared front half of the two attention entry points: the partials of query tokens
+// j0 .. j0 + Tq - 1 of a call with Tq_all tokens (j0 = 0, Tq_all = Tq for a single pass).
 dcp_status run_partials(const dcp_attn_shape* sh, int32_t Tq, const void* q, const void* k,
                         const void* v, const int32_t* block_table, const int32_t* bounds,
                         float* part_o, float* part_lse, void* workspace, size_t workspace_bytes,
-                        void* stream, dcp::Plan* plan_out, dcp::AttnArgs* args_out, bool fused) {
+                        void* stream, dcp::Plan* plan_out, dcp::AttnArgs* args_out, bool fused,
+                        int32_t j0 = 0, int32_t Tq_all = 0) {
+  if (Tq_all == 0) Tq_all = Tq;
   dcp::Plan plan;
   dcp_status st = make_plan(sh, Tq, &plan);
   if (st != DCP_OK) return st;
@@ -246,6 +258,8 @@ dcp_status run_partials(const dcp_attn_shape* sh, int32_t Tq, const void* q, con
   a.U = plan.units;
   a.Tq = Tq;
   a.R = sh->num_q_heads * Tq;
+  a.Rs = sh->num_q_heads * Tq_all;
+  a.j0 = j0;
   a.Ru = plan.rows_per_unit;
   a.NRg = plan.row_groups;
   a.scale_log2 = sh->softmax_scale * 1.4426950408889634f;
@@ -261,7 +275,7 @@ dcp_status run_partials(const dcp_attn_shape* sh, int32_t Tq, const void* q, con
   e = dcp::launch_schedule(bounds, a.B, a.S, units_per_bs, a.P,
                            reinterpret_cast<int32_t*>(ws + plan.ws.fin), a.bs, a.max_blocks,
                            const_cast<int32_t*>(a.ubounds), const_cast<int32_t*>(a.pre), a.flags,
-                           Tq, const_cast<int32_t*>(a.qend), a.redo,
+                           Tq_all, const_cast<int32_t*>(a.qend), a.redo,
                            const_cast<int32_t*>(a.usrc), s);
   if (e != hipSuccess) return device_fail(e, "schedule launch");
   const bool timed = g_timing.on && g_timing.used < g_timing.start.size();
@@ -350,7 +364,18 @@ dcp_status dcp_workspace_bytes_multi(const dcp_attn_shape* shape, int32_t q_len,
   dcp::Plan plan;
   dcp_status st = make_plan(shape, q_len, &plan);
   if (st != DCP_OK) return st;
-  *bytes = plan.ws.total;
+  size_t total = plan.ws.total;
+  // a fused call that runs in two passes reuses the workspace for each
+  const int32_t ta = split_tokens(shape, q_len);
+  if (ta > 0) {
+    for (const int32_t t : {ta, q_len - ta}) {
+      dcp::Plan p2;
+      st = make_plan(shape, t, &p2);
+      if (st != DCP_OK) return st;
+      if (p2.ws.total > total) total = p2.ws.total;
+    }
+  }
+  *bytes = total;
   return ok();
 }
 
@@ -402,13 +427,27 @@ dcp_status dcp_decode_attn_multi(const dcp_attn_shape* shape, int32_t q_len, con
                                  float* out_lse, void* stream) {
   if (!out) return fail(DCP_ERR_NULL, "out must be non-NULL");
   if (!aligned16(out)) return fail(DCP_ERR_ALIGN, "out must be 16-byte aligned");
-  dcp::Plan plan;
-  dcp::AttnArgs a;
-  dcp_status st = run_partials(shape, q_len, q, k_cache, v_cache, block_table, bounds, nullptr,
-                               nullptr, workspace, workspace_bytes, stream, &plan, &a, true);
-  if (st != DCP_OK) return st;
-  hipError_t e = dcp::launch_combine(a, out, out_lse, as_stream(stream));
-  if (e != hipSuccess) return device_fail(e, "combine launch");
+  {
+    dcp::Plan p0;  // the shape and q_len checks, before the pass split reads them
+    const dcp_status st = make_plan(shape, q_len, &p0);
+    if (st != DCP_OK) return st;
+  }
+  // one pass, or two (see split_tokens) run one after the other on the stream, each writing
+  // its own rows of out and out_lse; the second reuses the workspace after the first's combine
+  const int32_t ta = split_tokens(shape, q_len);
+  const int32_t passes = ta > 0 ? 2 : 1;
+  for (int32_t i = 0; i < passes; ++i) {
+    const int32_t j0 = i == 0 ? 0 : ta;
+    const int32_t t = passes == 1 ? q_len : (i == 0 ? ta : q_len - ta);
+    dcp::Plan plan;
+    dcp::AttnArgs a;
+    dcp_status st = run_partials(shape, t, q, k_cache, v_cache, block_table, bounds, nullptr,
+                                 nullptr, workspace, workspace_bytes, stream, &plan, &a, true,
+                                 j0, q_len);
+    if (st != DCP_OK) return st;
+    hipError_t e = dcp::launch_combine(a, out, out_lse, as_stream(stream));
+    if (e != hipSuccess) return device_fail(e, "combine launch");
+  }
   return ok();
 }
 

@@ -88,8 +88,17 @@ struct AttnArgs {
   const char* zero_row;     // kWsZeroWords*4 bytes of zeros in the workspace
   int32_t B, S, Hq, Hkv, G, Dqk, Dv, bs, max_blocks, num_blocks, U, P;
   int32_t Tq, R, Ru, NRg;   // query tokens, rows per request, rows per unit, groups per KV head
+  // A call may run its query tokens in passes: this pass takes tokens j0 .. j0 + Tq - 1 of the
+  // request's Tq_all, whose q, out and out_lse rows are Rs = Hq * Tq_all apart per request
+  // (Rs = R and j0 = 0 for a single pass). The partials in the workspace use the pass's R.
+  int32_t Rs, j0;
   float scale_log2;         // softmax_scale * log2(e)
 };
+
+// Row of the caller's q / out / out_lse for row rho of this pass of request b.
+__host__ __device__ inline int64_t call_row(const AttnArgs& a, int32_t b, int32_t rho) {
+  return (int64_t)b * a.Rs + (int64_t)a.j0 * a.Hq + rho;
+}
 
 // Query row of local row `r` of row group `rg` of KV head `kvh` (see "Query rows" above):
 // returns rho, or -1 for a padding row; *j receives the query token.

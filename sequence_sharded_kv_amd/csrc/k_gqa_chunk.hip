@@ -129,7 +129,7 @@ gqa_chunk_kernel(AttnArgs a) {
     int32_t jq = 0;
     const int32_t rho = unit_row(a, kvh, rg, 32 * wv + c32, &jq);
     const bool row_ok = rho >= 0;
-    const int32_t lim = (a.Tq == 1 || !row_ok) ? INT32_MAX : a.qend[b] + jq;
+    const int32_t lim = (a.Rs == a.Hq || !row_ok) ? INT32_MAX : a.qend[b] + a.j0 + jq;
 
     // Block ids of the segment's pages, 64 at a time: lane j holds the id of page pchunk + j.
     int32_t pchunk = -1, pid = -1;
@@ -189,7 +189,7 @@ gqa_chunk_kernel(AttnArgs a) {
     // Q^T as the B operand: lane holds q[row][16 ks + 8 g .. +8]
     bf16x8 qop[8];
     {
-      const uint16_t* qrow = Q + ((int64_t)b * a.R + (row_ok ? rho : 0)) * kD + 8 * g;
+      const uint16_t* qrow = Q + call_row(a, b, row_ok ? rho : 0) * kD + 8 * g;
       u32x4 raw[8];
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) raw[ks] = *(const u32x4*)(qrow + 16 * ks);

@@ -114,11 +114,11 @@ gqa_mfma_kernel(AttnArgs a) {
     int32_t jq = 0;
     const int32_t rho = unit_row(a, kvh, rg, n, &jq);
     const bool hv = rho >= 0;
-    const int32_t lim = a.Tq == 1 ? INT32_MAX : a.qend[b] + jq;
+    const int32_t lim = a.Rs == a.Hq ? INT32_MAX : a.qend[b] + a.j0 + jq;
     // Q^T as the B operand: lane (n, gq) holds q[rho][32j + 8gq .. +8]
     bf16x8 qop[C::kSteps];
     {
-      const uint16_t* qrow = Q + ((int64_t)b * a.R + (hv ? rho : 0)) * D;
+      const uint16_t* qrow = Q + call_row(a, b, hv ? rho : 0) * D;
 #pragma unroll
       for (int j = 0; j < C::kSteps; ++j) {
         u32x4 raw = *(const u32x4*)(qrow + 32 * j + 8 * gq);

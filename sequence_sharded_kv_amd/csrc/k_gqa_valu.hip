@@ -98,7 +98,7 @@ gqa_valu_kernel(AttnArgs a) {
       int h = i / D, d = i % D;
       int32_t jh = 0;
       const int32_t rho = unit_row(a, kvh, rg, h, &jh);
-      qs[i] = rho >= 0 ? Elem<T>::get(Q, ((int64_t)b * a.R + rho) * a.Dqk + d) : 0.f;
+      qs[i] = rho >= 0 ? Elem<T>::get(Q, call_row(a, b, rho) * a.Dqk + d) : 0.f;
     }
     // last context position each row may see (several query tokens)
     int32_t lim[kValuMaxG];
@@ -106,7 +106,7 @@ gqa_valu_kernel(AttnArgs a) {
     for (int h = 0; h < kValuMaxG; ++h) {
       int32_t jh = 0;
       const bool ok = unit_row(a, kvh, rg, h, &jh) >= 0;
-      lim[h] = (a.Tq == 1 || !ok) ? INT32_MAX : a.qend[b] + jh;
+      lim[h] = (a.Rs == a.Hq || !ok) ? INT32_MAX : a.qend[b] + a.j0 + jh;
     }
     __builtin_amdgcn_wave_barrier();
     float m[kValuMaxG], lsum[kValuMaxG], acc[kValuMaxG][NDV];

@@ -184,12 +184,12 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row, const int32_t* __
     int32_t jq = 0;
     const int32_t rho = unit_row(a, 0, rg, 16 * wv + n, &jq);
     const bool row_ok = rho >= 0;
-    const int32_t lim = a.Tq == 1 ? INT32_MAX
-                                  : __builtin_amdgcn_readfirstlane(a.qend[b] + jq);
+    const int32_t lim = a.Rs == a.Hq ? INT32_MAX
+                                  : __builtin_amdgcn_readfirstlane(a.qend[b] + a.j0 + jq);
     // the wave's Q slice as the B operand: lane holds q[row][32j + 8gq .. +8]
     bf16x8 qop[kMlaDqk / 32];
     {
-      const uint16_t* qrow = Q + ((int64_t)b * a.R + (row_ok ? rho : 0)) * kMlaDqk + 8 * gq;
+      const uint16_t* qrow = Q + call_row(a, b, row_ok ? rho : 0) * kMlaDqk + 8 * gq;
 #pragma unroll
       for (int j = 0; j < kMlaDqk / 32; ++j)
         qop[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 32 * j));

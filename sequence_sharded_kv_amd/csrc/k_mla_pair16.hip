@@ -206,12 +206,12 @@ mla_pair16_kernel(AttnArgs a, const char* __restrict__ zero_row, int32_t* __rest
     // This wave's 16 query rows and the last context position they may see.
     int32_t jq = 0;
     const int32_t rho_s = unit_row(a, 0, rg, 16 * wv + n, &jq);
-    const int32_t lim = a.Tq == 1 ? INT32_MAX
-                                  : __builtin_amdgcn_readfirstlane(a.qend[b] + jq);
+    const int32_t lim = a.Rs == a.Hq ? INT32_MAX
+                                  : __builtin_amdgcn_readfirstlane(a.qend[b] + a.j0 + jq);
     bf16x8 qop[kMlaDqk / 32];
     {
       const uint16_t* qrow =
-          Q + ((int64_t)b * a.R + (rho_s >= 0 ? rho_s : 0)) * kMlaDqk + 8 * gq;
+          Q + call_row(a, b, rho_s >= 0 ? rho_s : 0) * kMlaDqk + 8 * gq;
 #pragma unroll
       for (int j = 0; j < kMlaDqk / 32; ++j)
         qop[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 32 * j));

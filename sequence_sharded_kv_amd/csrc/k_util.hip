@@ -477,8 +477,9 @@ combine_kernel(AttnArgs a, float* __restrict__ out, float* __restrict__ out_lse)
   }
   if (!live || t != 0) return;
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  *(f32x4*)(out + br * a.Dv + 4 * c4) = acc * inv;
-  if (out_lse && c4 == 0) out_lse[br] = den > 0.f ? m + logf(den) : kNegInf;
+  const int64_t orow = call_row(a, b, rho);  // the caller's row (a pass may start at j0 > 0)
+  *(f32x4*)(out + orow * a.Dv + 4 * c4) = acc * inv;
+  if (out_lse && c4 == 0) out_lse[orow] = den > 0.f ? m + logf(den) : kNegInf;
 }
 
 hipError_t launch_combine(const AttnArgs& a, float* out, float* out_lse, hipStream_t stream) {

@@ -61,8 +61,10 @@ def test_kernel_family_follows_the_row_count(bench):
     assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=32), 1) == "mla"
     assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=32), 2) == "mla-ring"
     assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=16), 3) == "mla-ring"
+    assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=32), 5) == "mla-split"
+    assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=16), 12) == "mla-split"
     assert bench.kernel_family(workload("mla-64h-b512"), 2) == "mla-pair"   # 128 rows, 8 waves
-    assert bench.kernel_family(workload("mla-64h-b512"), 3) == "mla-ring"   # 3 x 64 rows
+    assert bench.kernel_family(workload("mla-64h-b512"), 3) == "mla-split"   # 128 + 64 rows
     assert bench.kernel_family(workload("mla-64h-b512"), 4) == "mla-pair"   # 2 x 128 rows
     assert bench.kernel_family(workload("mla-128h"), 1) == "mla-pair"
     assert bench.kernel_family(workload("mla-64h-b512").replace(num_q_heads=16), 5) == "mla-pair"

@@ -26,9 +26,13 @@ def _q_device(wl, qh):
 # name, workload, lengths, q_len, overrides
 CASES = [
     ("mla-64h-t2", "mla-64h-b512", [2000, 1, 700], 2, dict(batch=3)),
-    ("mla-64h-t3-three-groups", "mla-64h-b512", [1500, 64, 2], 3, dict(batch=3)),
-    # 192 rows: three 64-row units of two tokens each
-    ("mla-32h-t6-three-groups", "mla-64h-b512", [800, 90], 6, dict(batch=2, num_q_heads=32)),
+    # 129 to 192 rows: the partial call runs three 64-row units; the fused call two passes,
+    # 128 rows through the 128-row kernel and the rest through a smaller unit
+    ("mla-64h-t3-split", "mla-64h-b512", [1500, 64, 2], 3, dict(batch=3)),
+    ("mla-32h-t6-split", "mla-64h-b512", [800, 90], 6, dict(batch=2, num_q_heads=32)),
+    # second pass of 32 rows (the 16-rows-per-wave kernel), requests shorter than q_len
+    ("mla-32h-t5-split-32", "mla-64h-b512", [700, 130, 3], 5, dict(batch=3, num_q_heads=32)),
+    ("mla-16h-t10-split", "mla-64h-b512", [500, 9], 10, dict(batch=2, num_q_heads=16)),
     ("mla-16h-t8", "mla-64h-b512", [900, 8, 3], 8, dict(batch=3, num_q_heads=16)),
     ("mla-128h-t2", "mla-128h", [1200, 33], 2, dict(batch=2)),
     ("mla-32h-t3-padding", "mla-64h-b512", [600, 97], 3, dict(batch=2, num_q_heads=32)),
