@@ -276,7 +276,7 @@ dcp_status run_partials(const dcp_attn_shape* sh, int32_t Tq, const void* q, con
                            reinterpret_cast<int32_t*>(ws + plan.ws.fin), a.bs, a.max_blocks,
                            const_cast<int32_t*>(a.ubounds), const_cast<int32_t*>(a.pre), a.flags,
                            Tq_all, const_cast<int32_t*>(a.qend), a.redo,
-                           const_cast<int32_t*>(a.usrc), s);
+                           const_cast<int32_t*>(a.usrc), j0 > 0 ? 1 : 0, s);
   if (e != hipSuccess) return device_fail(e, "schedule launch");
   const bool timed = g_timing.on && g_timing.used < g_timing.start.size();
   if (timed) {

@@ -117,7 +117,7 @@ hipError_t launch_schedule(const int32_t* bounds, int32_t B, int32_t S, int32_t 
                            int32_t P, int32_t* fin,
                            int32_t bs, int32_t max_blocks, int32_t* ubounds, int32_t* pre,
                            int32_t* flags, int32_t Tq, int32_t* qend, int32_t* redo,
-                           int32_t* usrc, hipStream_t stream);
+                           int32_t* usrc, int32_t keep_flags, hipStream_t stream);
 hipError_t launch_finish_units(const AttnArgs& a, hipStream_t stream);
 // out / out_lse straight from the pieces and partials (fused calls; no finishing pass)
 hipError_t launch_combine(const AttnArgs& a, float* out, float* out_lse, hipStream_t stream);

@@ -48,7 +48,7 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
                 int32_t P, int32_t* __restrict__ fin, int32_t bs, int32_t max_blocks,
                 int32_t* __restrict__ ubounds, int32_t* __restrict__ pre,
                 int32_t* __restrict__ flags, int32_t Tq, int32_t* __restrict__ qend,
-                int32_t* __restrict__ redo, int32_t* __restrict__ usrc) {
+                int32_t* __restrict__ redo, int32_t* __restrict__ usrc, int32_t keep_flags) {
   __shared__ int32_t warp_sums[kSchedThreads / 64];
   __shared__ int32_t carry;
   __shared__ int32_t flag_acc;
@@ -178,7 +178,8 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
   }
   __syncthreads();
   if (tid == 0) {
-    flags[0] = flag_acc;
+    // a later pass of the same call keeps what the earlier passes flagged
+    flags[0] = keep_flags ? (flags[0] | flag_acc) : flag_acc;
     flags[1] = fin_count;
   }
 }
@@ -186,10 +187,11 @@ schedule_kernel(const int32_t* __restrict__ bounds, int32_t B, int32_t S, int32_
 hipError_t launch_schedule(const int32_t* bounds, int32_t B, int32_t S, int32_t units_per_bs,
                            int32_t P, int32_t* fin, int32_t bs, int32_t max_blocks,
                            int32_t* ubounds, int32_t* pre, int32_t* flags, int32_t Tq,
-                           int32_t* qend, int32_t* redo, int32_t* usrc, hipStream_t stream) {
+                           int32_t* qend, int32_t* redo, int32_t* usrc, int32_t keep_flags,
+                           hipStream_t stream) {
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, bounds, B, S,
                      units_per_bs, P, fin, bs, max_blocks, ubounds, pre, flags, Tq, qend, redo,
-                     usrc);
+                     usrc, keep_flags);
   return hipGetLastError();
 }
 

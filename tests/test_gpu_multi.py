@@ -441,3 +441,41 @@ def test_multi_row_kernels_flag_invalid_device_values(wl_name, over, lengths, T)
     torch.cuda.synchronize()
     assert dcp.dcp_read_device_flags(ws) & 1
     assert torch.isfinite(out).all()
+
+
+def test_two_pass_call_keeps_the_first_pass_flags():
+    """64 heads x 3 tokens run as a 128-row pass (fp16 value product) and a 64-row pass. With
+    one request's latent rows scaled below 2^-10, the first pass recomputes its workers in
+    bf16 (flag bit 2); the second pass must not clear that bit, and the outputs match the
+    oracle."""
+    from workloads import bf16_bits_from_f32
+    say("[gpu] two-pass call keeps the first pass's flags")
+    T = 3
+    wl = workload("mla-64h-b512").replace(batch=2)
+    lengths = [900, 400]
+    host = make_host_inputs(wl, lengths=lengths)
+    bs = wl.block_size
+    cache = host["kv_cache"]
+    pages = host["block_table"][1, : -(-lengths[1] // bs)]
+    vals = (cache[pages].astype(np.uint32) << 16).view(np.float32)
+    cache[pages] = bf16_bits_from_f32((vals * 2.0 ** -12).astype(np.float32))
+    inp = to_device(wl, host)
+    sh = shape_of(wl, inp)
+    B, S, Hq, Dv = wl.batch, wl.num_shards, wl.num_q_heads, wl.head_dim_v
+    qh = make_queries(wl, T)
+    q = _q_device(wl, qh)
+    bounds_np = dcp.dcp_plan_shards(host["seq_lens"], S, bs)
+    bounds = torch.from_numpy(bounds_np).cuda()
+    ws = dcp.alloc_workspace(sh, "cuda", T)
+    out = torch.empty((B, T, Hq, Dv), dtype=torch.float32, device="cuda")
+    out_lse = torch.empty((B, T, Hq), dtype=torch.float32, device="cuda")
+    dcp.dcp_decode_attn_multi(sh, T, q, inp["kv_cache"], None, inp["block_table"], bounds, ws,
+                              out, out_lse)
+    torch.cuda.synchronize()
+    assert dcp.dcp_read_device_flags(ws) & 4
+    _, caches, bt, _ = host_inputs_of(wl, inp)
+    ro, rl = O.partial_attention_multi(wl.kind, wl.dtype, qh, caches, bt,
+                                       np.asarray(bounds_np, np.int64), bs, wl.softmax_scale, Dv)
+    fo, fl = O.merge_lse(ro.reshape(B, S, T * Hq, Dv), rl.reshape(B, S, T * Hq))
+    assert_close(out.cpu().numpy().reshape(B, T * Hq, Dv), out_lse.cpu().numpy().reshape(B, T * Hq),
+                 fo, fl, wl.dtype, "two-pass tiny values")
