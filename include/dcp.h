@@ -250,12 +250,15 @@ dcp_status dcp_decode_attn_multi(const dcp_attn_shape* shape, int32_t q_len, con
  * dcp_read_device_flags -- copy the sticky device-side flag word out of a workspace and
  * wait for `stream`. Bit 0: a bound was clamped into [0, max_blocks_per_seq*block_size] or
  * had end < start. Bit 1: a block id outside [0, num_blocks) was met and its tokens masked.
- * Bit 2 (informational, results unaffected): on the MLA path with 128 query rows per unit, a
- * score exceeded its segment's first-tile maximum by more than 2^64 in weight, and that
- * worker's range was recomputed by the general kernel. Bit 3 (informational, results
- * unaffected): on the MLA path with 64 query rows per unit, the same happened and that worker
- * raised the row's reference and rescaled its sum and accumulator in place. Bits are cleared
- * by the next attention call on that workspace.
+ * Bit 2 (informational, results unaffected): on the MLA path with 128 query rows per unit,
+ * whose value product runs in fp16, a worker met a latent value of magnitude 65504 or more, or
+ * a segment whose nonzero values all stay below 2^-10, and its range was recomputed in bf16 by
+ * the general kernel. Bit 3 (informational, results unaffected): on the MLA paths with 64 or
+ * 128 query rows per unit or on the GQA bf16 head-dim-128 path, a tile's scores exceeded a
+ * row's reference (the maximum of its first tile with a visible token) by more than the
+ * weights' margin, and the row's reference was raised and its sum and accumulator rescaled in
+ * place. Bits are cleared by the next attention call on that workspace; a fused call that
+ * runs in two passes reports the bits of both.
  */
 dcp_status dcp_read_device_flags(const void* workspace, int32_t* flags, void* stream);
 
