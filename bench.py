@@ -93,8 +93,8 @@ def kernel_family(wl, q_len=1):
         # kernel, smaller units the 16-rows-per-wave kernel
         rows = q_len * wl.num_q_heads
         if 128 < rows <= 192:
-            # fused calls run two passes: 128 rows through the pair kernel, the rest (at most
-            # 64) through the ring kernel
+            # two passes: 128 rows through the pair kernel, the rest (at most 64) through the
+            # ring kernel
             return "mla-split"
         return "mla-pair" if rows > 64 else "mla-ring" if rows > 32 else "mla"
     g = wl.num_q_heads // wl.num_kv_heads

@@ -227,11 +227,10 @@ dcp_status dcp_decode_attn_noalloc(const dcp_attn_shape* shape, const void* q,
  * rows (q_len * Hq) in one pass, GQA up to 256 rows (q_len * Hq / Hkv) per KV head for bf16
  * head dim 128 and 16 for the other GQA shapes; a prefill
  * chunk therefore streams each shard's pages once per row group, as a flash-attention query
- * block does. MLA calls of 129 to 192 rows stream the pages three times in 64-row groups
- * through dcp_decode_attn_multi_partial, and twice through dcp_decode_attn_multi, which runs
- * the first 128 rows and the remaining tokens as two passes over the same workspace, one
- * after the other on the stream. The fused call keeps B * S * q_len * Hq partials in the
- * workspace (those of one pass at a time). Errors
+ * block does. MLA calls of 129 to 192 rows stream the pages twice: the first 128 rows and the
+ * remaining tokens run as two passes over the same workspace, one after the other on the
+ * stream, each writing its own rows of the outputs. The fused call keeps B * S * q_len * Hq
+ * partials in the workspace (those of one pass at a time). Errors
  * additionally: DCP_ERR_SHAPE for q_len outside [1, 4096].
  */
 dcp_status dcp_workspace_bytes_multi(const dcp_attn_shape* shape, int32_t q_len, size_t* bytes);

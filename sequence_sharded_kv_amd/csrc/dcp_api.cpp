@@ -141,8 +141,8 @@ dcp_status make_plan(const dcp_attn_shape* sh, int32_t Tq, dcp::Plan* plan) {
     // waves of 16 rows, a power of two of them up to 8 per workgroup
     ru = 16;
     while (ru < rows && ru < 128) ru *= 2;
-    // 129 to 192 rows: three 64-row units stream the KV faster than two of 128 rows whose
-    // second is at least half padding
+    // 129 to 192 rows: the calls run two passes (split_tokens); this single-pass plan of
+    // three 64-row units only enters the workspace size
     if (rows > 128 && rows <= 192) ru = 64;
     // units of 64 or 128 rows run one workgroup per CU (256 on gfx950), smaller ones two
     pmax = ru >= 64 ? kMaxWorkersMla / 2 : kMaxWorkersMla;
@@ -191,7 +191,7 @@ dcp_status device_fail(hipError_t e, const char* what) {
   return fail(DCP_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Fused MLA calls of 129 to 192 query rows run in two passes over the KV: the first 128 rows
+// MLA calls of 129 to 192 query rows run in two passes over the KV: the first 128 rows
 // (128 / Hq tokens) as one 128-row unit, the remaining tokens as one unit of at most 64 rows.
 // Returns the first pass's token count, or 0 where the call runs in one pass.
 int32_t split_tokens(const dcp_attn_shape* sh, int32_t Tq) {
@@ -260,6 +260,8 @@ dcp_status run_partials(const dcp_attn_shape* sh, int32_t Tq, const void* q, con
   a.R = sh->num_q_heads * Tq;
   a.Rs = sh->num_q_heads * Tq_all;
   a.j0 = j0;
+  a.Rp = fused ? a.R : a.Rs;  // the fused calls keep each pass's partials in the workspace
+  a.rp0 = fused ? 0 : j0 * sh->num_q_heads;
   a.Ru = plan.rows_per_unit;
   a.NRg = plan.row_groups;
   a.scale_log2 = sh->softmax_scale * 1.4426950408889634f;
@@ -365,7 +367,7 @@ dcp_status dcp_workspace_bytes_multi(const dcp_attn_shape* shape, int32_t q_len,
   dcp_status st = make_plan(shape, q_len, &plan);
   if (st != DCP_OK) return st;
   size_t total = plan.ws.total;
-  // a fused call that runs in two passes reuses the workspace for each
+  // a call that runs in two passes reuses the workspace for each
   const int32_t ta = split_tokens(shape, q_len);
   if (ta > 0) {
     for (const int32_t t : {ta, q_len - ta}) {
@@ -388,11 +390,25 @@ dcp_status dcp_decode_attn_multi_partial(const dcp_attn_shape* shape, int32_t q_
                                          const int32_t* block_table, const int32_t* bounds,
                                          float* part_o, float* part_lse, void* workspace,
                                          size_t workspace_bytes, void* stream) {
-  dcp::Plan plan;
-  dcp::AttnArgs a;
-  dcp_status st = run_partials(shape, q_len, q, k_cache, v_cache, block_table, bounds, part_o,
-                               part_lse, workspace, workspace_bytes, stream, &plan, &a, false);
-  return st == DCP_OK ? ok() : st;
+  {
+    dcp::Plan p0;  // the shape and q_len checks, before the pass split reads them
+    const dcp_status st = make_plan(shape, q_len, &p0);
+    if (st != DCP_OK) return st;
+  }
+  // one pass, or two (see split_tokens), each writing its own rows of part_o and part_lse
+  const int32_t ta = split_tokens(shape, q_len);
+  const int32_t passes = ta > 0 ? 2 : 1;
+  for (int32_t i = 0; i < passes; ++i) {
+    const int32_t j0 = i == 0 ? 0 : ta;
+    const int32_t t = passes == 1 ? q_len : (i == 0 ? ta : q_len - ta);
+    dcp::Plan plan;
+    dcp::AttnArgs a;
+    const dcp_status st = run_partials(shape, t, q, k_cache, v_cache, block_table, bounds, part_o,
+                                       part_lse, workspace, workspace_bytes, stream, &plan, &a,
+                                       false, j0, q_len);
+    if (st != DCP_OK) return st;
+  }
+  return ok();
 }
 
 dcp_status dcp_decode_attn_partial(const dcp_attn_shape* shape, const void* q,

@@ -90,14 +90,21 @@ struct AttnArgs {
   int32_t Tq, R, Ru, NRg;   // query tokens, rows per request, rows per unit, groups per KV head
   // A call may run its query tokens in passes: this pass takes tokens j0 .. j0 + Tq - 1 of the
   // request's Tq_all, whose q, out and out_lse rows are Rs = Hq * Tq_all apart per request
-  // (Rs = R and j0 = 0 for a single pass). The partials in the workspace use the pass's R.
-  int32_t Rs, j0;
+  // (Rs = R and j0 = 0 for a single pass). Partial rows of (request, shard) bsi sit Rp rows
+  // apart from row rp0 on: the caller's rows for the partial calls (Rp = Rs, rp0 = j0 * Hq),
+  // the pass's own rows in the workspace for the fused calls (Rp = R, rp0 = 0).
+  int32_t Rs, j0, Rp, rp0;
   float scale_log2;         // softmax_scale * log2(e)
 };
 
 // Row of the caller's q / out / out_lse for row rho of this pass of request b.
 __host__ __device__ inline int64_t call_row(const AttnArgs& a, int32_t b, int32_t rho) {
   return (int64_t)b * a.Rs + (int64_t)a.j0 * a.Hq + rho;
+}
+
+// Row of part_o / part_lse for row rho of this pass of (request, shard) bsi.
+__host__ __device__ inline int64_t part_row(const AttnArgs& a, int64_t bsi, int32_t rho) {
+  return bsi * a.Rp + a.rp0 + rho;
 }
 
 // Query row of local row `r` of row group `rg` of KV head `kvh` (see "Query rows" above):

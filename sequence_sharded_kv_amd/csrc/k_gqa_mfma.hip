@@ -261,8 +261,8 @@ gqa_mfma_kernel(AttnArgs a) {
     float* dst_o;
     float* dst_l;
     if (whole) {
-      dst_o = a.part_o + ((int64_t)bsi * a.R + rho) * D;
-      dst_l = a.part_lse + (int64_t)bsi * a.R + rho;
+      dst_o = a.part_o + part_row(a, bsi, rho) * D;
+      dst_l = a.part_lse + part_row(a, bsi, rho);
     } else {
       int32_t slot = piece_slot(w, first);
       dst_o = a.piece_o + ((int64_t)slot * a.Ru + n) * D;

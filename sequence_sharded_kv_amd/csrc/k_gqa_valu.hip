@@ -198,9 +198,9 @@ gqa_valu_kernel(AttnArgs a) {
       int32_t jh = 0;
       const int32_t rho = unit_row(a, kvh, rg, h, &jh);
       if (rho >= 0) {
-        float* dst_o = whole ? a.part_o + ((int64_t)bsi * a.R + rho) * a.Dv
+        float* dst_o = whole ? a.part_o + part_row(a, bsi, rho) * a.Dv
                              : a.piece_o + ((int64_t)slot * Ru + h) * a.Dv;
-        float* dst_l = whole ? a.part_lse + (int64_t)bsi * a.R + rho
+        float* dst_l = whole ? a.part_lse + part_row(a, bsi, rho)
                              : a.piece_lse + (int64_t)slot * Ru + h;
         float l = wave_sum(lsum[h]);
         float inv = l > 0.f ? 1.f / l : 0.f;

@@ -285,8 +285,8 @@ mla_mfma_kernel(AttnArgs a, const char* __restrict__ zero_row, const int32_t* __
     float* dst_o;
     float* dst_l;
     if (whole) {
-      dst_o = a.part_o + ((int64_t)bsi * a.R + rho) * kMlaDv;
-      dst_l = a.part_lse + (int64_t)bsi * a.R + rho;
+      dst_o = a.part_o + part_row(a, bsi, rho) * kMlaDv;
+      dst_l = a.part_lse + part_row(a, bsi, rho);
     } else {
       const int32_t slot = piece_slot(w, first);
       dst_o = a.piece_o + ((int64_t)slot * a.Ru + 16 * wv + n) * kMlaDv;

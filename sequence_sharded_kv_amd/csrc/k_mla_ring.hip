@@ -429,8 +429,8 @@ mla_ring_kernel(AttnArgs a, const char* __restrict__ zero_row) {
       float* dst_o;
       float* dst_l;
       if (whole) {
-        dst_o = a.part_o + ((int64_t)bsi * a.R + (rho >= 0 ? rho : 0)) * kMlaDv;
-        dst_l = a.part_lse + (int64_t)bsi * a.R + (rho >= 0 ? rho : 0);
+        dst_o = a.part_o + part_row(a, bsi, rho >= 0 ? rho : 0) * kMlaDv;
+        dst_l = a.part_lse + part_row(a, bsi, rho >= 0 ? rho : 0);
       } else {
         const int32_t slot = piece_slot(w, first);
         dst_o = a.piece_o + ((int64_t)slot * a.Ru + hrow) * kMlaDv;

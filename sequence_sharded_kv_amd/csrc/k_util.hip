@@ -224,8 +224,8 @@ finish_units_kernel(AttnArgs a) {
     const int32_t bsi = u / per_bs, hsub = u % per_bs;
     int32_t jtok = 0;
     const int32_t rho = (i4 < n4) ? unit_row(a, hsub / a.NRg, hsub % a.NRg, h, &jtok) : -1;
-    float* out_o = a.part_o + ((int64_t)bsi * a.R + (rho < 0 ? 0 : rho)) * a.Dv;
-    float* out_l = a.part_lse + (int64_t)bsi * a.R + (rho < 0 ? 0 : rho);
+    float* out_o = a.part_o + part_row(a, bsi, rho < 0 ? 0 : rho) * a.Dv;
+    float* out_l = a.part_lse + part_row(a, bsi, rho < 0 ? 0 : rho);
     if (w0 < 0) {
       if (rho >= 0) {
         ((f32x4*)out_o)[c4] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -426,7 +426,7 @@ combine_kernel(AttnArgs a, float* __restrict__ out, float* __restrict__ out_lse)
       l[c] = kNegInf;
       o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (s0 + c < a.S && (s0 + c) % kSplit == t) {
-        const int64_t row = ((int64_t)b * a.S + s0 + c) * a.R + rho;
+        const int64_t row = part_row(a, (int64_t)b * a.S + s0 + c, rho);
         l[c] = a.part_lse[row];
         o[c] = *(const f32x4*)(a.part_o + row * a.Dv + 4 * c4);
       }

@@ -26,8 +26,8 @@ def _q_device(wl, qh):
 # name, workload, lengths, q_len, overrides
 CASES = [
     ("mla-64h-t2", "mla-64h-b512", [2000, 1, 700], 2, dict(batch=3)),
-    # 129 to 192 rows: the partial call runs three 64-row units; the fused call two passes,
-    # 128 rows through the 128-row kernel and the rest through a smaller unit
+    # 129 to 192 rows: two passes, 128 rows through the 128-row kernel and the rest through a
+    # smaller unit, for the partial and the fused call
     ("mla-64h-t3-split", "mla-64h-b512", [1500, 64, 2], 3, dict(batch=3)),
     ("mla-32h-t6-split", "mla-64h-b512", [800, 90], 6, dict(batch=2, num_q_heads=32)),
     # second pass of 32 rows (the 16-rows-per-wave kernel), requests shorter than q_len
