@@ -252,12 +252,15 @@ def test_multi_token_shapes_and_errors():
                                      None) == dcp.DCP_ERR_SHAPE
     assert lib.dcp_decode_attn_multi_partial(ctypes.byref(sh), 2, A, A, None, A, A, None, A, A,
                                              need, None) == dcp.DCP_ERR_NULL
+    # a two-pass call (64 heads x 3 tokens) checks the workspace before its first launch
+    assert lib.dcp_decode_attn_multi_partial(ctypes.byref(sh), 3, A, A, None, A, A, A, A, A,
+                                             need - 1, None) == dcp.DCP_ERR_WORKSPACE
 
 
 def test_workspace_of_a_two_pass_call_holds_each_pass():
-    """Fused MLA calls of 129 to 192 query rows run a 128-row pass (128 / Hq tokens) and a
-    pass with the remaining tokens in the same workspace: the size reported for the call
-    covers the single-pass plans of both token counts."""
+    """MLA calls of 129 to 192 query rows run a 128-row pass (128 / Hq tokens) and a pass
+    with the remaining tokens in the same workspace: the size reported for the call covers
+    the single-pass plans of both token counts."""
     for hq, q_len in ((64, 3), (32, 5), (32, 6), (16, 9), (16, 12)):
         sh = _shape(num_q_heads=hq)
         ta = 128 // hq
